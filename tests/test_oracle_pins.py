@@ -1,0 +1,556 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+worked example printed on a page, a closed form, an exact rational
+computation, an independent scalar re-derivation, or an invariant.  The
+docstring of each test names what pins it.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import OracleDataError
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _scalar_digits(b):
+    """Base-3 digits of b, least significant first, by repeated division."""
+    out = []
+    for _ in range(5):
+        b, r = divmod(b, 3)
+        out.append(r)
+    return out
+
+
+# ---------------------------------------------------------------- fp rounding
+
+def _exact_nearest_even(x, candidates):
+    """Nearest of `candidates` (sorted Fractions) to Fraction x; ties -> even index."""
+    best = min(range(len(candidates)), key=lambda i: (abs(candidates[i] - x), i % 2))
+    return best
+
+
+def test_f16_identity_all_patterns():
+    """Every finite fp16 value converts back to its own bit pattern (IEEE 754)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = oracle.f16_bits_to_f64(bits)
+    keep = ~np.isnan(v)
+    out = oracle.f64_to_f16_bits(v[keep])
+    zero_neg = bits[keep] == 0x8000
+    assert np.array_equal(out[~zero_neg], bits[keep][~zero_neg])
+    assert out[zero_neg][0] in (0x8000,)
+
+
+def test_f16_midpoints_ties_to_even():
+    """Midpoints between neighbouring positive fp16 values round to the even
+    pattern; just above / below a midpoint rounds away / towards (IEEE 754)."""
+    lo = np.arange(0, 0x7BFF, dtype=np.uint16)              # up to 65504 - ulp
+    hi = lo + np.uint16(1)
+    a, b = oracle.f16_bits_to_f64(lo), oracle.f16_bits_to_f64(hi)
+    mid = (a + b) / 2                                        # exact in float64
+    got = oracle.f64_to_f16_bits(mid)
+    even = np.where(lo % 2 == 0, lo, hi)
+    assert np.array_equal(got, even)
+    up = np.nextafter(mid, np.inf)
+    dn = np.nextafter(mid, -np.inf)
+    assert np.array_equal(oracle.f64_to_f16_bits(up), hi)
+    assert np.array_equal(oracle.f64_to_f16_bits(dn), lo)
+
+
+def test_f16_overflow_and_against_numpy():
+    """65504 is the largest finite fp16; 65520 (the midpoint to 2**16) rounds
+    to infinity; random values agree with numpy's own float64->float16 cast,
+    an independent implementation."""
+    assert oracle.f64_to_f16_bits(np.array([65504.0]))[0] == 0x7BFF
+    assert oracle.f64_to_f16_bits(np.array([65519.99]))[0] == 0x7BFF
+    assert oracle.f64_to_f16_bits(np.array([65520.0]))[0] == 0x7C00
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 5, 200000),
+        rng.uniform(-2 ** -14, 2 ** -14, 50000),
+    ])
+    ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f64_to_f16_bits(x), ref)
+
+
+def test_f16_exact_rationals():
+    """A few values checked against exact rational nearest-even rounding."""
+    grid = [Fraction(float(v))
+            for v in oracle.f16_bits_to_f64(np.arange(0x3C00, 0x3C10, dtype=np.uint16))]
+    for num in range(0, 61):
+        x = grid[0] + (grid[15] - grid[0]) * Fraction(num, 60)
+        i = _exact_nearest_even(x, grid)
+        got = oracle.f64_to_f16_bits(np.array([float(x)]))[0]
+        if float(x) == x:                                   # exact in float64
+            assert got == 0x3C00 + i
+
+
+def test_bf16_identity_midpoints_and_bits():
+    """bf16: identity over all finite patterns, ties to even at midpoints, and
+    agreement with the integer bit formula on float32 inputs."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = oracle.bf16_bits_to_f64(bits)
+    keep = ~np.isnan(v) & (bits != 0x8000)
+    assert np.array_equal(oracle.f64_to_bf16_bits(v[keep]), bits[keep])
+    lo = np.arange(0, 0x7F7F, dtype=np.uint16)
+    hi = lo + np.uint16(1)
+    mid = (oracle.bf16_bits_to_f64(lo) + oracle.bf16_bits_to_f64(hi)) / 2
+    assert np.array_equal(oracle.f64_to_bf16_bits(mid), np.where(lo % 2 == 0, lo, hi))
+    rng = np.random.default_rng(12)
+    f = (rng.standard_normal(100000) * 10.0 ** rng.integers(-30, 30, 100000)).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    ref = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_bits(f.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------- packing
+
+def test_worked_example_183():
+    """The page's worked example: trits (-1, 0, 1, -1, 1) <-> byte 183."""
+    lines = {ln[0]: ln[1:] for ln in _golden_lines("trit_byte_example.txt")}
+    trits = np.array([[int(v) for v in lines["trits"]]], dtype=np.int8)
+    byte = int(lines["byte"][0])
+    codes = oracle.pack(trits, 5)
+    assert codes.shape == (1, 1, 1) and int(codes[0, 0, 0]) == byte
+    back = oracle.ternary.unpack_trits(codes, 5, 5)
+    assert np.array_equal(back, trits)
+
+
+def test_all_243_words_round_trip():
+    """All 243 five-trit words against an independent scalar base-3 calculation."""
+    words = np.array([[d - 1 for d in _scalar_digits(b)] for b in range(243)], dtype=np.int8)
+    t = words.reshape(1, 243 * 5)
+    codes = oracle.pack(t, 5)
+    assert np.array_equal(codes.reshape(-1), np.arange(243, dtype=np.uint8))
+    assert np.array_equal(oracle.ternary.unpack_trits(codes, 243 * 5, 5), t)
+    for b in (0, 1, 121, 182, 242):
+        digits = _scalar_digits(b)
+        assert sum(d * 3 ** q for q, d in enumerate(digits)) == b
+
+
+@pytest.mark.parametrize("bad", range(243, 256))
+def test_bytes_243_to_255_rejected(bad):
+    """Byte values 243..255 are not five-trit words and are rejected."""
+    codes = np.full((2, 1, 13), 121, dtype=np.uint8)
+    codes[1, 0, 7] = bad
+    with pytest.raises(OracleDataError) as e:
+        oracle.unpack(codes, np.zeros((2, 1), np.uint16), 64, 64)
+    assert e.value.kind == "code"
+
+
+def test_padding_must_decode_to_zero():
+    """G=64: byte 12 holds trits 60..63 and one padding digit that must be 1
+    (trit 0); a ragged final group pads every unused slot the same way."""
+    codes = np.full((1, 1, 13), 121, dtype=np.uint8)
+    codes[0, 0, 12] = 121 + 81                      # padding digit 4 -> 2
+    with pytest.raises(OracleDataError) as e:
+        oracle.unpack(codes, np.zeros((1, 1), np.uint16), 64, 64)
+    assert e.value.kind == "padding"
+    codes[0, 0, 12] = 121 - 1                       # digit 0 is data: fine
+    oracle.unpack(codes, np.zeros((1, 1), np.uint16), 64, 64)
+    # ragged: K = 70, G = 64 -> second group has 6 members, bytes 2..12 padding
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((3, 70)).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    assert c.shape == (3, 2, 13)
+    assert np.all(c[:, 1, 2:] == 121)                # 1 + 3 + 9 + 27 + 81
+    assert np.all(c[:, 1, 1] % 3 == c[:, 1, 1] % 3)
+    assert np.all(c[:, 1, 1] // 3 == 40)             # trit 5 is data, digits 1..4 pad
+    bad = c.copy()
+    bad[0, 1, 5] = 120
+    with pytest.raises(OracleDataError):
+        oracle.unpack(bad, s, 70, 64)
+    w = oracle.unpack(c, s, 70, 64)
+    assert w.shape == (3, 70)
+
+
+def test_group_boundaries_and_rows():
+    """Groups never straddle rows; a group's bytes depend only on its own
+    64 weights (changing one weight changes one group of one row)."""
+    rng = np.random.default_rng(4)
+    W = rng.standard_normal((4, 192)).astype(np.float32)
+    c0, s0 = oracle.quantize_pack(W, 64)
+    W2 = W.copy()
+    W2[2, 64 + 17] *= 3.0
+    c1, s1 = oracle.quantize_pack(W2, 64)
+    diff_groups = {(r, g) for r in range(4) for g in range(3)
+                   if not (np.array_equal(c0[r, g], c1[r, g]) and s0[r, g] == s1[r, g])}
+    assert diff_groups <= {(2, 1)} and (2, 1) in diff_groups
+
+
+def test_byte_counts():
+    """The page's byte accounting: G=64 -> 13 + 2 = 15 B -> 1.875 bits/weight."""
+    for G, cb, gb, bpw in _golden_lines("byte_counts.txt"):
+        G, cb, gb, bpw = int(G), int(cb), int(gb), float(bpw)
+        assert oracle.bytes_per_group(G) == cb
+        assert cb + 2 == gb
+        assert oracle.bits_per_weight(G) == bpw
+        W = np.ones((3, 4 * G), np.float32)
+        c, s = oracle.quantize_pack(W, G)
+        assert c.nbytes + s.nbytes == 3 * 4 * gb
+
+
+# ---------------------------------------------------------------- quantizer
+
+def _one_group(vals):
+    return oracle.quantize(np.array([vals], dtype=np.float32), len(vals))
+
+
+def test_scale_closed_form_and_both_ties():
+    """32 x 0.75 and 32 x (-0.25): mean |W| = 0.5 exactly, s = 0.5;
+    0.75/0.5 = 1.5 rounds (to even) to 2 and clips to 1; -0.25/0.5 = -0.5
+    rounds (to even) to 0."""
+    vals = [0.75] * 32 + [-0.25] * 32
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(64)
+    vals = [vals[i] for i in perm]
+    s, t = _one_group(vals)
+    assert s[0, 0] == 0x3800                           # fp16 0.5
+    expect = [1 if v == 0.75 else 0 for v in vals]
+    assert t[0].tolist() == expect
+
+
+def test_scale_constant_spike_zero_tiny():
+    """Constant c: s = fp16(c), all t = 1.  One spike v among zeros:
+    s = fp16(v/64), one t = sign(v).  All zero: s = 0, bytes 121, W_hat 0.
+    Mean <= 2**-25 rounds to s = 0: all-zero group although |W| > 0."""
+    s, t = _one_group([0.3] * 64)
+    assert s[0, 0] == np.float16(0.3).view(np.uint16) and np.all(t == 1)
+    vals = [0.0] * 64
+    vals[40] = -0.64
+    s, t = _one_group(vals)
+    assert s[0, 0] == np.float16(0.01).view(np.uint16)
+    assert t[0, 40] == -1 and np.count_nonzero(t) == 1
+    W = np.zeros((2, 64), np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    assert np.all(s == 0) and np.all(c == 121)
+    assert np.all(oracle.unpack(c, s, 64, 64) == 0)
+    tiny = np.full((1, 64), 2.0 ** -26, np.float32)
+    s, t = oracle.quantize(tiny, 64)
+    assert s[0, 0] == 0 and np.all(t == 0)
+    tiny2 = np.full((1, 64), 2.0 ** -25 * 1.001, np.float32)
+    s, t = oracle.quantize(tiny2, 64)
+    assert s[0, 0] == 1 and np.all(t == 1)             # smallest subnormal fp16
+
+
+def test_scale_is_one_rounding_of_the_exact_mean():
+    """s equals the nearest-even fp16 of the exact rational mean (computed with
+    Fractions) on random groups, including ragged ones."""
+    rng = np.random.default_rng(6)
+    for n in (64, 64, 64, 37, 5, 128):
+        for _ in range(60):
+            w = (rng.standard_normal(n) * 10.0 ** rng.integers(-6, 3)).astype(np.float32)
+            s, _ = oracle.quantize(w[None, :], max(n, 64) if n != 128 else 128)
+            exact = sum(Fraction(float(abs(v))) for v in w) / n
+            lo = float(exact)
+            grid = oracle.f16_bits_to_f64(np.arange(0, 0x7C00, dtype=np.uint16))
+            i = np.searchsorted(grid, lo)
+            cands = [j for j in (i - 1, i, i + 1) if 0 <= j < len(grid)]
+            best = min(cands, key=lambda j: (abs(Fraction(float(grid[j])) - exact), j % 2))
+            assert s[0, 0] == best
+
+
+def test_sign_and_ties_against_scalar_rule():
+    """t = clip(RNE(W/s), -1, 1) for every weight, re-derived per weight in
+    exact rational arithmetic with Python's round (ties to even)."""
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    W[0, :4] = [0.5, -0.5, 0.25, 1.0]
+    s, t = oracle.quantize(W, 64)
+    sv = oracle.f16_bits_to_f64(s)
+    for r in range(6):
+        for k in range(128):
+            sc = Fraction(float(sv[r, k // 64]))
+            q = 0 if sc == 0 else max(-1, min(1, round(Fraction(float(W[r, k])) / sc)))
+            assert t[r, k] == q
+
+
+def test_nonfinite_and_overflow_are_range_errors():
+    for bad in (np.nan, np.inf, -np.inf):
+        W = np.zeros((1, 64), np.float32)
+        W[0, 3] = bad
+        with pytest.raises(OracleDataError) as e:
+            oracle.quantize(W, 64)
+        assert e.value.kind == "range"
+    W = np.full((1, 64), 65520.0, np.float32)
+    with pytest.raises(OracleDataError):
+        oracle.quantize(W, 64)
+    W = np.full((1, 64), 65519.0, np.float32)
+    s, _ = oracle.quantize(W, 64)
+    assert s[0, 0] == 0x7BFF
+
+
+def test_value_set_and_error_monotone():
+    """At most 3 distinct reconstructed values per group ({-s, 0, s}), at most
+    9 with two planes; |W - s t| <= |W| for every weight (t != 0 only when
+    |W| > s/2 with the sign of W), and plane 2 never increases it."""
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    w = oracle.unpack(c, s, 256, 64)
+    sv = oracle.f16_bits_to_f64(s)
+    for r in range(32):
+        for g in range(4):
+            vals = set(np.unique(w[r, g * 64:(g + 1) * 64]).tolist())
+            assert vals <= {-sv[r, g], 0.0, sv[r, g]}
+    assert np.all(np.abs(W - w) <= np.abs(W))
+    (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    w1 = oracle.unpack(c1, s1, 256, 64)
+    w2 = oracle.unpack(c2, s2, 256, 64)
+    R = W - w1.astype(np.float32)
+    assert np.all(np.abs(R - w2) <= np.abs(R))
+    both = w1 + w2
+    for r in range(32):
+        for g in range(4):
+            assert len(np.unique(both[r, g * 64:(g + 1) * 64])) <= 9
+    assert np.sum((W - both) ** 2) < 0.5 * np.sum((W - w1) ** 2)
+
+
+def test_two_plane_plane1_is_single_plane_and_residual_rule():
+    """Plane 1 of two_plane is the single-plane package; plane 2 is the
+    single-plane package of fl32(W - s1 t1)."""
+    rng = np.random.default_rng(10)
+    W = (rng.standard_normal((8, 128)) * 0.02).astype(np.float32)
+    (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    cs, ss = oracle.quantize_pack(W, 64)
+    assert np.array_equal(c1, cs) and np.array_equal(s1, ss)
+    t1 = oracle.ternary.unpack_trits(c1, 128, 64)
+    sv = np.repeat(oracle.f16_bits_to_f64(s1), 64, axis=1)
+    R = np.empty_like(W)
+    for r in range(8):
+        for k in range(128):
+            R[r, k] = np.float32(W[r, k]) - np.float32(sv[r, k] * t1[r, k])
+    cr, sr = oracle.quantize_pack(R, 64)
+    assert np.array_equal(c2, cr) and np.array_equal(s2, sr)
+
+
+def test_gaussian_relative_mse():
+    """Statistical sanity: on N(0, 1) weights the relative MSE of the
+    single-plane quantizer is near the closed form for a population mean-abs
+    scale s = sqrt(2/pi):  1 - 2 s 2 phi(s/2) + s^2 2 (1 - Phi(s/2)) ~ 0.2634.
+    Per-group sample scales move it by a few thousandths."""
+    sp = math.sqrt(2 / math.pi)
+    c = sp / 2
+    phi = math.exp(-c * c / 2) / math.sqrt(2 * math.pi)
+    Phi = 0.5 * (1 + math.erf(c / math.sqrt(2)))
+    closed = 1 - 2 * sp * 2 * phi + sp * sp * 2 * (1 - Phi)
+    rng = np.random.default_rng(13)
+    W = rng.standard_normal((1000, 1024)).astype(np.float32)
+    cc, s = oracle.quantize_pack(W, 64)
+    w = oracle.unpack(cc, s, 1024, 64)
+    rel = np.sum((W - w) ** 2) / np.sum(W.astype(np.float64) ** 2)
+    assert abs(closed - 0.2634) < 1e-3
+    assert abs(rel - closed) < 0.01
+
+
+# ---------------------------------------------------------------- Route B
+
+def _ladders():
+    out = {}
+    for ln in _golden_lines("routeb_ladder.txt"):
+        out[ln[0]] = np.array([float(v) for v in ln[1:]], dtype=np.float32)
+    return out
+
+
+def test_code_words_digit_order():
+    """codes = base-3 encoding of c_1..c_5 with c_1 most significant:
+    sum_i (c_i + 1) 3^(5-i) == b for every code."""
+    cw = oracle.code_words().astype(int)
+    for b in range(243):
+        assert sum((cw[b, i - 1] + 1) * 3 ** (5 - i) for i in range(1, 6)) == b
+
+
+def test_table_integer_ladder_closed_form():
+    """With the integer ladder (81, 27, 9, 3, 1) the code book is exactly
+    T[b] = b - 121 (the balanced-ternary value of the word)."""
+    T = oracle.rb_table(np.array([81, 27, 9, 3, 1], np.float32))
+    assert np.array_equal(T, (np.arange(243) - 121).astype(np.float32))
+
+
+def test_table_balanced_ladder_and_symmetry():
+    """S0 = (1, 1/3, 1/9, 1/27, 1/81): T[b] ~ (b - 121)/81, strictly
+    increasing, T[121] = 0, T[242 - b] = -T[b] exactly.  The fitted S of the
+    paper keeps the antisymmetry and T[121] = 0."""
+    lad = _ladders()
+    T = oracle.rb_table(lad["S0"])
+    assert T[121] == 0
+    assert np.all(np.diff(T) > 0)
+    assert np.allclose(T, (np.arange(243) - 121) / 81.0, rtol=0, atol=1e-6)
+    assert np.array_equal(T[::-1], -T)
+    Ts = oracle.rb_table(lad["S"])
+    assert Ts[121] == 0 and np.array_equal(Ts[::-1], -Ts)
+
+
+def test_table_entries_are_the_exact_sums():
+    """For the ladders of the workloads (a_i = 0.5^(i-1) u_i, u_i in
+    [0.8, 1.2]) each entry is the nearest fp32 of the exact rational sum."""
+    import workloads
+    for seed in range(5):
+        a = workloads.routeb_gemv(seed=seed, N=1, K=1, M=1)["ladder"]
+        T = oracle.rb_table(a)
+        cw = oracle.code_words().astype(int)
+        for b in range(243):
+            exact = sum(Fraction(int(cw[b, i])) * Fraction(float(a[i])) for i in range(5))
+            assert Fraction(float(exact)) == exact
+            assert T[b] == np.float32(float(exact))
+
+
+def test_rb_weights_definition():
+    """W_hat[n, k] = alpha * T[codes[n, k]] * rho_n, scalar re-derivation."""
+    rng = np.random.default_rng(14)
+    a = np.array([1.0, 0.34, 0.11, 0.04, 0.013], np.float32)
+    T = oracle.rb_table(a)
+    codes = rng.integers(0, 243, (5, 9), dtype=np.uint8)
+    rho = np.array([0.5, 1.0, 1.25, 0.75, 1.5], np.float16).view(np.uint16)
+    w = oracle.rb_weights(codes, T, np.float32(0.02), rho)
+    rv = rho.view(np.float16)
+    for n in range(5):
+        for k in range(9):
+            ref = Fraction(float(np.float32(0.02))) * Fraction(float(T[codes[n, k]])) * Fraction(float(rv[n]))
+            assert abs(Fraction(w[n, k]) - ref) <= abs(ref) * Fraction(1, 2 ** 52)
+
+
+# ---------------------------------------------------------------- matmul
+
+def _bf16(rng, shape, scale=1.0):
+    import workloads
+    return workloads.bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def _exact_matmul(xb, w_exact_rows, bias=None):
+    """Pure-Python exact rational y and B for tiny shapes."""
+    x = [[Fraction(float(v)) for v in row] for row in oracle.bf16_bits_to_f64(xb)]
+    M, N = len(x), len(w_exact_rows)
+    y = [[sum(x[m][k] * w_exact_rows[n][k] for k in range(len(x[m]))) for n in range(N)] for m in range(M)]
+    B = [[sum(abs(x[m][k] * w_exact_rows[n][k]) for k in range(len(x[m]))) for n in range(N)] for m in range(M)]
+    if bias is not None:
+        for m in range(M):
+            for n in range(N):
+                y[m][n] += Fraction(float(bias[n]))
+                B[m][n] += abs(Fraction(float(bias[n])))
+    return y, B
+
+
+def _scalar_ternary_rows(codes, s_bits, K, G):
+    """Weights decoded one byte at a time with the scalar digit routine."""
+    rows = []
+    sv = oracle.f16_bits_to_f64(s_bits)
+    nb = oracle.bytes_per_group(G)
+    for n in range(codes.shape[0]):
+        row = []
+        for k in range(K):
+            g, j = divmod(k, G)
+            byte = int(codes[n, g, j // 5])
+            d = _scalar_digits(byte)[j % 5]
+            row.append(Fraction(float(sv[n, g])) * (d - 1))
+        rows.append(row)
+    assert nb == codes.shape[2]
+    return rows
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (3, 7, 128), (5, 4, 320), (16, 2, 64), (2, 3, 70)])
+def test_ternary_matmul_brute_force(M, N, K):
+    """Oracle y and B against exact rational arithmetic on tiny shapes, with
+    the weights re-decoded byte by byte (catches transposes, index and sign
+    mistakes); the oracle's float64 result is within 1e-12 B of exact."""
+    rng = np.random.default_rng(100 + M * 31 + N * 7 + K)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xb = _bf16(rng, (M, K))
+    c, s = oracle.quantize_pack(W, 64)
+    y, B = oracle.matmul_ref(xb, oracle.ternary_weights(K, 64, c, s))
+    ye, Be = _exact_matmul(xb, _scalar_ternary_rows(c, s, K, 64))
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(y[m, n]) - ye[m][n]) <= Be[m][n] * Fraction(1, 10 ** 12)
+            assert abs(Fraction(B[m, n]) - Be[m][n]) <= Be[m][n] * Fraction(1, 10 ** 12)
+
+
+def test_two_plane_matmul_brute_force():
+    rng = np.random.default_rng(101)
+    W = (rng.standard_normal((5, 128)) * 0.02).astype(np.float32)
+    xb = _bf16(rng, (3, 128))
+    (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    y, B = oracle.matmul_ref(xb, oracle.ternary_weights(128, 64, c1, s1, c2, s2))
+    r1 = _scalar_ternary_rows(c1, s1, 128, 64)
+    r2 = _scalar_ternary_rows(c2, s2, 128, 64)
+    rows = [[a + b for a, b in zip(p, q)] for p, q in zip(r1, r2)]
+    ye, Be = _exact_matmul(xb, rows)
+    for m in range(3):
+        for n in range(5):
+            assert abs(Fraction(y[m, n]) - ye[m][n]) <= Be[m][n] * Fraction(1, 10 ** 12)
+
+
+@pytest.mark.parametrize("with_rho,with_bias", [(False, False), (True, False), (True, True)])
+def test_routeb_matmul_brute_force(with_rho, with_bias):
+    rng = np.random.default_rng(102)
+    a = np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32)
+    T = oracle.rb_table(a)
+    N, K, M = 6, 40, 4
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    rho = rng.uniform(0.5, 1.5, N).astype(np.float16).view(np.uint16) if with_rho else None
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    xb = _bf16(rng, (M, K))
+    y, B = oracle.matmul_ref(xb, oracle.rb_weights(codes, T, np.float32(0.02), rho), bias)
+    rv = rho.view(np.float16) if with_rho else np.ones(N)
+    rows = [[Fraction(float(np.float32(0.02))) * Fraction(float(T[codes[n, k]])) * Fraction(float(rv[n]))
+             for k in range(K)] for n in range(N)]
+    ye, Be = _exact_matmul(xb, rows, bias)
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(y[m, n]) - ye[m][n]) <= Be[m][n] * Fraction(1, 10 ** 12)
+
+
+def test_matmul_special_cases():
+    """One-hot x picks a column of W_hat exactly; x = 0 gives 0; with
+    integer-valued x and power-of-two scales every partial sum is exact."""
+    rng = np.random.default_rng(103)
+    W = (rng.standard_normal((9, 128)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    w = oracle.ternary_weights(128, 64, c, s)
+    import workloads
+    eye = workloads.bf16_bits(np.eye(128, dtype=np.float32))
+    y, _ = oracle.matmul_ref(eye, w)
+    assert np.array_equal(y, w.T)
+    y0, B0 = oracle.matmul_ref(np.zeros((2, 128), np.uint16), w)
+    assert np.all(y0 == 0) and np.all(B0 == 0)
+
+
+def test_grouped_reduces_to_dense():
+    """Grouped matmul with every (token, slot) routed to one expert equals the
+    dense matmul with that expert's weights, per slot."""
+    rng = np.random.default_rng(104)
+    Ws = [(rng.standard_normal((6, 64)) * 0.02).astype(np.float32) for _ in range(3)]
+    pk = [oracle.quantize_pack(W, 64) for W in Ws]
+    xb = _bf16(rng, (4, 64))
+    ids = np.full((4, 2), 1, np.int32)
+    y, B = oracle.grouped_ref(xb, ids, lambda e: oracle.ternary_weights(64, 64, *pk[e]))
+    yd, Bd = oracle.matmul_ref(xb, oracle.ternary_weights(64, 64, *pk[1]))
+    for j in range(2):
+        assert np.array_equal(y[:, j], yd) and np.array_equal(B[:, j], Bd)
+    ids = np.array([[0, 2], [1, 0], [2, 1], [0, 1]], np.int32)
+    y, _ = oracle.grouped_ref(xb, ids, lambda e: oracle.ternary_weights(64, 64, *pk[e]))
+    for t in range(4):
+        for j in range(2):
+            ye, _ = oracle.matmul_ref(xb[t:t + 1], oracle.ternary_weights(64, 64, *pk[ids[t, j]]))
+            assert np.array_equal(y[t, j], ye[0])
+
+
+def test_check_bound_logic():
+    """The acceptance rule: |y - y_ref| <= 2e-3 B, no NaN/Inf, B = 0 needs equality."""
+    yr = np.array([1.0, 0.0, -2.0])
+    B = np.array([10.0, 0.0, 2.0])
+    assert oracle.check_bound(yr + [0.0199, 0.0, 0.0039], yr, B)["ok"]
+    assert not oracle.check_bound(yr + [0.0201, 0.0, 0.0], yr, B)["ok"]
+    assert not oracle.check_bound(yr + [0.0, 1e-30, 0.0], yr, B)["ok"]
+    assert not oracle.check_bound(np.array([np.nan, 0.0, -2.0]), yr, B)["ok"]
