@@ -1,0 +1,203 @@
+"""Python binding of libdecode_matmul.so (packed ternary-code matmul, gfx950).
+
+Argument marshalling only: each function below has the name of a C entry
+point of include/decode_matmul.h, checks that the torch tensors it is handed
+have the dtype, device, contiguity and size the C call will touch, passes raw
+device pointers and the current HIP stream, and raises RuntimeError on a
+non-zero status.  All arithmetic runs in the HIP kernels.  PyTorch supplies
+device memory and streams.
+
+If the shared library has not been built, importing this package raises
+ImportError: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdecode_matmul.so")
+
+TQ_OK = 0
+TQ_F32 = 0
+TQ_BF16 = 1
+TQ_DATA_RANGE = 1
+TQ_DATA_CODE = 2
+TQ_DATA_PADDING = 4
+
+EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_matmul", "tq_status_string")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m decode_matmul_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+_lib.tq_pack.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p]
+_lib.tq_unpack.argtypes = [_p, _p, _i64, _i64, _i32, _p, _i32, _p, _p]
+_lib.tq_matmul.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i64, _i32, _i32, _p, _i32, _p,
+                           _i32, _p]
+_lib.rb_table.argtypes = [_p, _p]
+_lib.rb_matmul.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _p, _p, _i32, _p]
+_lib.tq_status_string.argtypes = [_i32]
+_lib.tq_status_string.restype = ctypes.c_char_p
+for _name in ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_matmul"):
+    getattr(_lib, _name).restype = _i32
+
+
+def tq_status_string(status):
+    return _lib.tq_status_string(int(status)).decode()
+
+
+def _raise(rc, what):
+    if rc != TQ_OK:
+        raise RuntimeError(f"{what}: {tq_status_string(rc)} (status {rc})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtypes, numel, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+_U8 = (torch.uint8,)
+_H16 = (torch.float16, torch.int16, torch.uint16)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def packed_shape(rows, K, G):
+    """(codes shape, scales shape) of the package of a [rows, K] matrix."""
+    ng = -(-K // G)
+    return (rows, ng, -(-G // 5)), (rows, ng)
+
+
+def _ydtype(y):
+    if y.dtype == torch.float32:
+        return TQ_F32
+    if y.dtype in _BF16:
+        return TQ_BF16
+    raise TypeError(f"y dtype {y.dtype} must be float32 or bfloat16")
+
+
+def tq_pack(W, G, planes, codes1, scales1, codes2=None, scales2=None, status=None):
+    """Quantize and pack fp32 W [rows, K] into caller-allocated packages."""
+    dev = W.device
+    rows, K = W.shape
+    cs, ss = packed_shape(rows, K, G)
+    _need(W, "W", _F32, rows * K, dev)
+    _need(codes1, "codes1", _U8, cs[0] * cs[1] * cs[2], dev)
+    _need(scales1, "scales1", _H16, ss[0] * ss[1], dev)
+    if planes == 2:
+        _need(codes2, "codes2", _U8, cs[0] * cs[1] * cs[2], dev)
+        _need(scales2, "scales2", _H16, ss[0] * ss[1], dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(status, "status", _I32, 1, dev)
+    rc = _lib.tq_pack(_ptr(W), rows, K, G, planes, _ptr(codes1), _ptr(scales1), _ptr(codes2),
+                      _ptr(scales2), _ptr(status), _stream(dev))
+    _raise(rc, "tq_pack")
+    return status
+
+
+def tq_unpack(codes, scales, rows, K, G, W_out, status=None):
+    """Decode a package into W_out [rows, K] (float32 exact, or bfloat16)."""
+    dev = codes.device
+    cs, ss = packed_shape(rows, K, G)
+    _need(codes, "codes", _U8, cs[0] * cs[1] * cs[2], dev)
+    _need(scales, "scales", _H16, ss[0] * ss[1], dev)
+    if W_out.dtype == torch.float32:
+        odt = TQ_F32
+    elif W_out.dtype in _BF16:
+        odt = TQ_BF16
+    else:
+        raise TypeError("W_out must be float32 or bfloat16")
+    _need(W_out, "W_out", (W_out.dtype,), rows * K, dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(status, "status", _I32, 1, dev)
+    rc = _lib.tq_unpack(_ptr(codes), _ptr(scales), rows, K, G, _ptr(W_out), odt, _ptr(status),
+                        _stream(dev))
+    _raise(rc, "tq_unpack")
+    return status
+
+
+def tq_matmul(x, codes1, scales1, N, G, y, codes2=None, scales2=None, n_experts=0,
+              expert_ids=None, top_k=1):
+    """y = x W_hat^T; dense (n_experts=0) or grouped by expert_ids [M, top_k]."""
+    dev = x.device
+    M, K = x.shape
+    E = max(n_experts, 1)
+    cs, ss = packed_shape(N, K, G)
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes1, "codes1", _U8, E * cs[0] * cs[1] * cs[2], dev)
+    _need(scales1, "scales1", _H16, E * ss[0] * ss[1], dev)
+    if codes2 is not None or scales2 is not None:
+        _need(codes2, "codes2", _U8, E * cs[0] * cs[1] * cs[2], dev)
+        _need(scales2, "scales2", _H16, E * ss[0] * ss[1], dev)
+    if n_experts > 0:
+        _need(expert_ids, "expert_ids", _I32, M * top_k, dev)
+        _need(y, "y", (y.dtype,), M * top_k * N, dev)
+    else:
+        _need(y, "y", (y.dtype,), M * N, dev)
+    rc = _lib.tq_matmul(_ptr(x), M, K, _ptr(codes1), _ptr(scales1), _ptr(codes2), _ptr(scales2),
+                        N, G, n_experts, _ptr(expert_ids), top_k, _ptr(y), _ydtype(y),
+                        _stream(dev))
+    _raise(rc, "tq_matmul")
+
+
+def rb_table(ladder):
+    """Host: 243-entry fp32 code book of a 5-step ladder (numpy float32 arrays)."""
+    import numpy as np
+    a = np.ascontiguousarray(ladder, dtype=np.float32)
+    if a.shape != (5,):
+        raise ValueError("the ladder has five steps")
+    out = np.zeros(243, dtype=np.float32)
+    rc = _lib.rb_table(a.ctypes.data_as(_p), out.ctypes.data_as(_p))
+    _raise(rc, "rb_table")
+    return out
+
+
+def rb_matmul(x, codes, table, alpha, y, row_scale=None, bias=None):
+    """y = alpha * rho * (x T[codes]^T) + bias for uint8 codes [N, K]."""
+    dev = x.device
+    M, K = x.shape
+    N = codes.shape[0]
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes, "codes", _U8, N * K, dev)
+    _need(table, "table", _F32, 243, dev)
+    if row_scale is not None:
+        _need(row_scale, "row_scale", _H16, N, dev)
+    if bias is not None:
+        _need(bias, "bias", _F32, N, dev)
+    _need(y, "y", (y.dtype,), M * N, dev)
+    rc = _lib.rb_matmul(_ptr(x), M, K, _ptr(codes), N, _ptr(table), float(alpha),
+                        _ptr(row_scale), _ptr(bias), _ptr(y), _ydtype(y), _stream(dev))
+    _raise(rc, "rb_matmul")
+
+
+def raw():
+    """The ctypes handle, for callers that marshal pointers themselves."""
+    return _lib

@@ -1,0 +1,160 @@
+// extern "C" entry points: argument validation on the host, then launches on
+// the caller's stream.  No memory is allocated and no state is kept.
+#include <stddef.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool group_ok(int G) { return G == 64 || G == 128; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(int status) {
+    switch (status) {
+        case TQ_OK: return "ok";
+        case TQ_ERR_NULL: return "a required pointer is NULL";
+        case TQ_ERR_SHAPE: return "a size is negative, inconsistent or too large";
+        case TQ_ERR_UNSUPPORTED: return "unsupported group size, plane count or mode";
+        case TQ_ERR_DTYPE: return "unknown dtype";
+        case TQ_ERR_ALIGN: return "a pointer is not aligned as documented";
+        case TQ_ERR_HIP: return "the HIP runtime rejected a launch";
+        default: return "unknown status";
+    }
+}
+
+int tq_pack(const float* W, int64_t rows, int64_t K, int32_t G, int32_t planes,
+            uint8_t* codes1, uint16_t* scales1, uint8_t* codes2, uint16_t* scales2,
+            int32_t* d_status, void* stream) {
+    if (!W || !codes1 || !scales1 || !d_status) return TQ_ERR_NULL;
+    if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return TQ_ERR_SHAPE;
+    if (!group_ok(G) || (planes != 1 && planes != 2)) return TQ_ERR_UNSUPPORTED;
+    if (planes == 2 && (!codes2 || !scales2)) return TQ_ERR_NULL;
+    if (planes == 1 && (codes2 || scales2)) return TQ_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(scales1, 2) || (scales2 && !aligned(scales2, 2)) ||
+        !aligned(d_status, 4))
+        return TQ_ERR_ALIGN;
+    const int64_t groups = rows * ((K + G - 1) / G);
+    if (groups / 256 >= kMaxDim) return TQ_ERR_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dmm::launch_status_clear(d_status, s);
+    if (e != hipSuccess) return TQ_ERR_HIP;
+    return hip_status(dmm::launch_pack(W, rows, K, G, planes, codes1, scales1, codes2, scales2,
+                                       d_status, s));
+}
+
+int tq_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t K,
+              int32_t G, void* W_out, int32_t out_dtype, int32_t* d_status, void* stream) {
+    if (!codes || !scales || !W_out || !d_status) return TQ_ERR_NULL;
+    if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return TQ_ERR_SHAPE;
+    if (!group_ok(G)) return TQ_ERR_UNSUPPORTED;
+    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_ERR_DTYPE;
+    if (!aligned(scales, 2) || !aligned(W_out, out_dtype == TQ_F32 ? 4 : 2) ||
+        !aligned(d_status, 4))
+        return TQ_ERR_ALIGN;
+    const int64_t groups = rows * ((K + G - 1) / G);
+    if (groups / 256 >= kMaxDim) return TQ_ERR_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dmm::launch_status_clear(d_status, s);
+    if (e != hipSuccess) return TQ_ERR_HIP;
+    return hip_status(dmm::launch_unpack(codes, scales, rows, K, G, W_out, out_dtype, d_status, s));
+}
+
+int tq_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
+              const uint16_t* scales1, const uint8_t* codes2, const uint16_t* scales2,
+              int64_t N, int32_t G, int32_t n_experts, const int32_t* expert_ids,
+              int32_t top_k, void* y, int32_t y_dtype, void* stream) {
+    if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
+        return TQ_ERR_SHAPE;
+    if (!group_ok(G)) return TQ_ERR_UNSUPPORTED;
+    if (K % G != 0) return TQ_ERR_SHAPE;
+    if (y_dtype != TQ_F32 && y_dtype != TQ_BF16) return TQ_ERR_DTYPE;
+    if (n_experts < 0) return TQ_ERR_SHAPE;
+    if ((codes2 == nullptr) != (scales2 == nullptr)) return TQ_ERR_NULL;
+    if (n_experts > 0) {
+        if (top_k < 1) return TQ_ERR_SHAPE;
+        if (M * (int64_t)top_k > dmm::tq_max_grouped_pairs()) return TQ_ERR_SHAPE;
+    }
+    if (M == 0 || N == 0) return TQ_OK;
+    if (!y || (K > 0 && (!x || !codes1 || !scales1))) return TQ_ERR_NULL;
+    if (n_experts > 0 && !expert_ids) return TQ_ERR_NULL;
+    if (!aligned(x, 4) || !aligned(scales1, 2) || (scales2 && !aligned(scales2, 2)) ||
+        !aligned(y, y_dtype == TQ_F32 ? 4 : 2) || (expert_ids && !aligned(expert_ids, 4)))
+        return TQ_ERR_ALIGN;
+    const int64_t row_blocks = (N + 15) / 16;
+    if (row_blocks * (n_experts > 0 ? n_experts : 1) >= kMaxDim) return TQ_ERR_SHAPE;
+    dmm::TqMatmulArgs a;
+    a.x = x;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.codes[0] = codes1;
+    a.codes[1] = codes2;
+    a.scales[0] = scales1;
+    a.scales[1] = scales2;
+    a.planes = codes2 ? 2 : 1;
+    a.G = G;
+    a.n_experts = n_experts;
+    a.ids = n_experts > 0 ? expert_ids : nullptr;
+    a.top_k = n_experts > 0 ? top_k : 1;
+    a.y = y;
+    a.y_dtype = y_dtype;
+    return hip_status(dmm::launch_tq_matmul(a, (hipStream_t)stream));
+}
+
+int rb_table(const float* ladder, float* table_out) {
+    if (!ladder || !table_out) return TQ_ERR_NULL;
+    for (int b = 0; b < 243; ++b) {
+        double acc = 0.0;
+        int p3 = 81;                               // 3^(5-i) for i = 1
+        for (int i = 0; i < 5; ++i) {
+            const int c = (b / p3) % 3 - 1;        // c_1 is the most significant digit
+            acc += (double)c * (double)ladder[i];
+            p3 /= 3;
+        }
+        table_out[b] = (float)acc;                 // one nearest-even rounding
+    }
+    return TQ_OK;
+}
+
+int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+              const float* table, float alpha, const uint16_t* row_scale, const float* bias,
+              void* y, int32_t y_dtype, void* stream) {
+    if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
+        return TQ_ERR_SHAPE;
+    if (y_dtype != TQ_F32 && y_dtype != TQ_BF16) return TQ_ERR_DTYPE;
+    if (M == 0 || N == 0) return TQ_OK;
+    if (!table || !y || (K > 0 && (!x || !codes))) return TQ_ERR_NULL;
+    if (!aligned(x, 2) || !aligned(table, 4) || (row_scale && !aligned(row_scale, 2)) ||
+        (bias && !aligned(bias, 4)) || !aligned(y, y_dtype == TQ_F32 ? 4 : 2))
+        return TQ_ERR_ALIGN;
+    dmm::RbMatmulArgs a;
+    a.x = x;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.codes = codes;
+    a.table = table;
+    a.alpha = alpha;
+    a.row_scale = row_scale;
+    a.bias = bias;
+    a.y = y;
+    a.y_dtype = y_dtype;
+    hipStream_t s = (hipStream_t)stream;
+    if (M <= 16) {
+        if ((N + 15) / 16 >= kMaxDim) return TQ_ERR_SHAPE;
+        return hip_status(dmm::launch_rb_gemv(a, s));
+    }
+    if ((M + 127) / 128 >= 65536) return TQ_ERR_SHAPE;
+    return hip_status(dmm::launch_rb_prefill(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Device helpers and internal launcher declarations of the packed-code
+// matmul library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_matmul.h"
+
+namespace dmm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte vectors loaded from 4-byte aligned addresses.
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);   // exact
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// fp32 -> bf16, nearest-even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// float64 -> fp16 bits, nearest-even, one rounding straight from the
+// float64 value (integer arithmetic on the bit pattern).
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+    uint64_t b = __builtin_bit_cast(uint64_t, x);
+    uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    uint64_t a = b & 0x7fffffffffffffffull;
+    if (a >= 0x7ff0000000000000ull)                       // inf or nan
+        return (uint16_t)(sign | (a > 0x7ff0000000000000ull ? 0x7e00u : 0x7c00u));
+    int e = (int)(a >> 52) - 1023;                         // binade of |x|
+    if (e > 15) return (uint16_t)(sign | 0x7c00u);         // >= 2^16
+    if (e < -25) return (uint16_t)sign;                    // < 2^-25 -> 0
+    uint64_t m = (a & 0x000fffffffffffffull) | 0x0010000000000000ull;
+    // spacing of fp16 at this binade: 2^(e-10) for normals, 2^-24 below 2^-14
+    int s = (e >= -14) ? 42 : (28 - e);                    // 42..53
+    uint64_t q = m >> s;
+    uint64_t rem = m & ((1ull << s) - 1ull);
+    uint64_t half = 1ull << (s - 1);
+    if (rem > half || (rem == half && (q & 1ull))) q += 1ull;
+    uint32_t bits = (e >= -14) ? (((uint32_t)(e + 15) << 10) + (uint32_t)(q - 1024ull))
+                               : (uint32_t)q;              // carries roll into exponent
+    return (uint16_t)(sign | bits);
+}
+
+// ------------------------------------------------------------ small ops
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Bytes [sh, sh+4) of the 8-byte little-endian value {hi:lo}, sh in 0..3.
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+
+__device__ __forceinline__ void atomic_or_status(int32_t* st, int32_t flag) {
+    if (st) atomicOr(st, flag);
+}
+
+// Wave-uniform read of an SGPR-able value.
+__device__ __forceinline__ int readfirstlane(int v) {
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+}  // namespace dmm
+
+// ------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; arguments were validated by
+// the C entry points.
+
+namespace dmm {
+
+hipError_t launch_status_clear(int32_t* d_status, hipStream_t s);
+
+hipError_t launch_pack(const float* W, int64_t rows, int64_t K, int G, int planes,
+                       uint8_t* c1, uint16_t* s1, uint8_t* c2, uint16_t* s2,
+                       int32_t* d_status, hipStream_t s);
+
+hipError_t launch_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows,
+                         int64_t K, int G, void* out, int out_dtype, int32_t* d_status,
+                         hipStream_t s);
+
+struct TqMatmulArgs {
+    const uint16_t* x;
+    int64_t M, K, N;
+    const uint8_t* codes[2];
+    const uint16_t* scales[2];
+    int planes;
+    int G;
+    int n_experts;          // 0 = dense
+    const int32_t* ids;     // [M, top_k] when grouped
+    int top_k;
+    void* y;
+    int y_dtype;
+};
+
+hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
+int tq_max_grouped_pairs();  // largest M * top_k of a grouped call
+
+struct RbMatmulArgs {
+    const uint16_t* x;
+    int64_t M, K, N;
+    const uint8_t* codes;
+    const float* table;
+    float alpha;
+    const uint16_t* row_scale;
+    const float* bias;
+    void* y;
+    int y_dtype;
+};
+
+hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s);
+hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s);
+
+}  // namespace dmm

@@ -1,0 +1,212 @@
+// Route B prefill (M > 16): y[m, n] = alpha * rho_n * sum_k x[m, k] T[codes[n, k]] + bias_n
+// as a bf16 MFMA GEMM whose weight tiles are decoded from code bytes into LDS.
+//
+// Semantics: "A Discrete Weight Language for Large Language Models" (Route
+// B), section 4.2: the code book is loaded on chip once per block and a
+// K-sliced GEMM dereferences every code byte through it; rho_n is applied to
+// the output accumulator before the bias add (section 3.3).
+//
+// Mapping onto gfx950:
+//  * 256-thread workgroups own a 128 x 128 tile of y (tokens x rows); 4 waves
+//    in a 2 x 2 grid each own 64 x 64 = 4 x 4 MFMA 16x16x32 tiles.
+//  * Per K-slice of 64: the activation tile is copied to LDS; the code tile
+//    (128 rows x 64 bytes) is decoded through a 32-copy bank-replicated LDS
+//    table of bf16 code-book values into a bf16 weight tile in LDS.  The
+//    next slice's global loads are issued before the current MFMAs.
+//  * Weight values are bf16 of the fp32 table entry (relative error <=
+//    2^-9 per term); accumulation is fp32.
+#include "common.h"
+
+namespace dmm {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDT = BK + 8;                  // LDS row pitch in bf16 (144 B)
+constexpr int kThreads = 256;
+constexpr int kCopies = 32;
+
+struct Params {
+    const uint16_t* x;
+    int64_t M, K, N;
+    const uint8_t* codes;
+    const float* table;
+    float alpha;
+    const uint16_t* row_scale;
+    const float* bias;
+    void* y;
+    int y_dtype;
+    int aligned;                             // x, codes 16-B aligned and K % 16 == 0
+};
+
+__global__ void __launch_bounds__(kThreads, 2)
+rb_prefill_kernel(Params p) {
+    __shared__ uint32_t lut[256 * kCopies];                     // 32 KB
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDT];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    for (int i = tid; i < 256 * kCopies; i += kThreads) {
+        const int b = i / kCopies;
+        lut[i] = b < 243 ? (uint32_t)f32_to_bf16_rne(p.table[b]) : 0u;
+    }
+
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int lr = tid >> 1;                 // tile row this thread loads
+    const int lh = tid & 1;                  // which 32-column half
+    const bool m_full = m0 + BM <= p.M;
+    const bool n_full = n0 + BN <= p.N;
+    // lane constant for the LUT address: copy (lane & 31), entry stride 128 B
+    const uint32_t lane_c = (uint32_t)(lane & 31) << 3;
+
+    u32x4 ra[4], rc[2];
+    auto gload = [&](int64_t k0) {
+        const bool full = p.aligned && m_full && n_full && (k0 + BK <= p.K);
+        const int64_t m = m0 + lr, n = n0 + lr;
+        const int64_t k = k0 + 32 * lh;
+        if (full) {
+            const u32x4* xp = (const u32x4*)(p.x + m * p.K + k);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ra[i] = xp[i];
+            const u32x4* cp = (const u32x4*)(p.codes + n * p.K + k);
+            rc[0] = cp[0];
+            rc[1] = cp[1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t kk = k + 8 * i + 2 * j;
+                    uint32_t lo = 0, hi = 0;
+                    if (m < p.M) {
+                        if (kk < p.K) lo = p.x[m * p.K + kk];
+                        if (kk + 1 < p.K) hi = p.x[m * p.K + kk + 1];
+                    }
+                    ra[i][j] = lo | (hi << 16);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int64_t kk = k + 16 * i + 4 * j + b;
+                        const uint32_t c = (n < p.N && kk < p.K) ? p.codes[n * p.K + kk] : 0xffu;
+                        w |= c << (8 * b);
+                    }
+                    rc[i][j] = w;
+                }
+            }
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const unsigned char* lutb = (const unsigned char*)lut;
+    gload(0);
+    for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
+        __syncthreads();                              // previous slice consumed
+        {
+            u32x4* ad = (u32x4*)(As + lr * LDT + 32 * lh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ad[i] = ra[i];
+            u32x4* bd = (u32x4*)(Bs + lr * LDT + 32 * lh);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = rc[i][j];
+                    uint32_t e[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t a2 = perm_b32(w, lane_c, 0x0c0c0400u + ((uint32_t)b << 8));
+                        e[b] = *(const uint32_t*)(lutb + (a2 >> 1));
+                    }
+                    const uint32_t p01 = perm_b32(e[1], e[0], 0x05040100u);
+                    const uint32_t p23 = perm_b32(e[3], e[2], 0x05040100u);
+                    ((uint32_t*)bd)[8 * i + 2 * j] = p01;
+                    ((uint32_t*)bd)[8 * i + 2 * j + 1] = p23;
+                }
+            }
+        }
+        __syncthreads();
+        if (k0 + BK < p.K) gload(k0 + BK);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int kc = kk * 32 + (lane >> 4) * 8;
+            u32x4 af[4], bfv[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                af[mb] = *(const u32x4*)(As + (wm * 64 + mb * 16 + (lane & 15)) * LDT + kc);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                bfv[nb] = *(const u32x4*)(Bs + (wn * 64 + nb * 16 + (lane & 15)) * LDT + kc);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, af[mb]), __builtin_bit_cast(bf16x8, bfv[nb]),
+                        acc[mb][nb], 0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
+        if (n >= p.N) continue;
+        const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
+        const float bias = p.bias ? p.bias[n] : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = m0 + wm * 64 + mb * 16 + 4 * (lane >> 4) + i;
+                if (m >= p.M) continue;
+                float v = acc[mb][nb][i] * rho;
+                v = v * p.alpha;
+                v = v + bias;
+                const int64_t idx = m * p.N + n;
+                if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
+                else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s) {
+    Params p;
+    p.x = a.x;
+    p.M = a.M;
+    p.K = a.K;
+    p.N = a.N;
+    p.codes = a.codes;
+    p.table = a.table;
+    p.alpha = a.alpha;
+    p.row_scale = a.row_scale;
+    p.bias = a.bias;
+    p.y = a.y;
+    p.y_dtype = a.y_dtype;
+    p.aligned = (((uintptr_t)a.x & 15) == 0) && (((uintptr_t)a.codes & 15) == 0) &&
+                (a.K % 16 == 0);
+    const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
+    if (gx == 0 || gy == 0) return hipSuccess;
+    hipLaunchKernelGGL(rb_prefill_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s,
+                       p);
+    return hipGetLastError();
+}
+
+}  // namespace dmm

@@ -1,0 +1,321 @@
+// Ternary GEMV: y = x (s1 T1 + s2 T2)^T over the mean-abs ternary package,
+// decoded inside the kernel.
+//
+// Format: "Does your weight format deserve a kernel?" (pack-unpack-run),
+// "Five trits in a byte" and "Three values and a shared scale"; the second
+// plane and the expert selection follow the FUCINA README ("The method",
+// "Runtime requirements").
+//
+// Mapping onto gfx950 (wave64, bf16 MFMA 16x16x32, fp32 accumulate):
+//
+//  * A workgroup owns 16 output rows (one MFMA column block) of one expert
+//    and splits the K groups over its waves; wave partials meet in LDS.
+//  * Each lane of a wave decodes one whole group of one row: lane l handles
+//    row (l & 15) and group 4*quad + (l >> 4).  The group's ceil(G/5) code
+//    bytes are fetched with aligned dword loads and realigned with
+//    v_alignbyte; each byte indexes a 256-entry LDS table that holds the
+//    five trits as the high bytes of bf16 values 2t (0x40 / 0x00 / 0xC0), and
+//    v_perm assembles bf16 pairs (2t_j, 2t_{j+1}) in natural trit order.
+//    Trits are exact in bf16; the factor 2 is folded into the group scale.
+//  * The MFMA A operand is block diagonal: A row r = 4 m + g' holds token m's
+//    activations for group g' in the K-slots of lane block g' and zeros
+//    elsewhere.  C[4 m + g', col] is then the partial sum of exactly one
+//    group, so the fp16 group scale is applied in fp32 after the MFMA (per
+//    group, as the format requires) at no extra MFMA cost for M <= 4.  More
+//    tokens run further token quads over the same decoded operands.
+//  * Activations are read straight from global memory (they are tiny and
+//    stay in L1/L2); codes stream from HBM once per token chunk of 16.
+#include "common.h"
+
+namespace dmm {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 16;          // tokens per pass over the codes
+constexpr int kMaxList = 4096;      // grouped mode: M * top_k limit
+
+struct Params {
+    const uint16_t* x;
+    int64_t K, N;
+    int ng;                          // groups per row
+    const uint8_t* codes0;
+    const uint8_t* codes1;
+    const uint16_t* scales0;
+    const uint16_t* scales1;
+    int planes;
+    int64_t code_stride;             // bytes per expert
+    int64_t scale_stride;            // scales per expert
+    int grouped;
+    const int32_t* ids;
+    int top_k;
+    int M;                           // tokens
+    int row_blocks;
+    void* y;
+    int y_dtype;
+};
+
+// bf16 high byte of 2t for digit d = t + 1.
+__device__ __forceinline__ uint32_t trit_hi_byte(int d) {
+    return d == 2 ? 0x40u : (d == 0 ? 0xC0u : 0x00u);
+}
+
+// Load the NB code bytes of one group starting at byte address p into
+// dwords D[0..ceil(NB/4)-1] (byte i of the group = byte i%4 of D[i/4]).
+// Only dwords that hold at least one byte of the group are read.
+template <int NB>
+__device__ __forceinline__ void load_group_bytes(const uint8_t* p, uint32_t* D) {
+    constexpr int ND = (NB + 3) / 4;
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    const uint32_t* aw = (const uint32_t*)(p - sh);      // keeps the global address space
+    uint32_t W[ND + 1];
+    if constexpr (NB == 13) {
+        // 13 bytes at offset sh <= 3 always fit the 16 aligned bytes.
+        u32x4a v = *(const u32x4a*)aw;
+        W[0] = v.x; W[1] = v.y; W[2] = v.z; W[3] = v.w; W[4] = 0;
+    } else {
+        static_assert(NB == 26, "G = 64 or 128");
+        u32x4a v = *(const u32x4a*)aw;
+        u32x3a u = *(const u32x3a*)(aw + 4);
+        W[0] = v.x; W[1] = v.y; W[2] = v.z; W[3] = v.w;
+        W[4] = u.x; W[5] = u.y; W[6] = u.z;
+        W[7] = (sh == 3) ? aw[7] : 0u;     // byte 25 sits in dword 7 only if sh == 3
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) D[i] = align_bytes(W[i + 1], W[i], sh);
+}
+
+// Decode one group (G trits) into G/2 bf16 pair registers, natural order.
+template <int G>
+__device__ __forceinline__ void decode_group(const uint8_t* p, const uint2* lut, uint32_t* B) {
+    constexpr int NB = (G + 4) / 5;
+    constexpr int ND = (NB + 3) / 4;
+    uint32_t D[ND];
+    load_group_bytes<NB>(p, D);
+    uint32_t Elo[NB], Ehi[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        uint32_t b = (D[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        uint2 e = lut[b];
+        Elo[i] = e.x;
+        Ehi[i] = e.y;
+    }
+#pragma unroll
+    for (int p2 = 0; p2 < G / 2; ++p2) {
+        const int ja = 2 * p2, jb = 2 * p2 + 1;
+        const int ia = ja / 5, qa = ja % 5, ib = jb / 5, qb = jb % 5;
+        const uint32_t ra = qa < 4 ? Elo[ia] : Ehi[ia];
+        const uint32_t rb = qb < 4 ? Elo[ib] : Ehi[ib];
+        const uint32_t ba = qa < 4 ? qa : 0, bb = qb < 4 ? qb : 0;
+        const bool same = (ia == ib) && ((qa < 4) == (qb < 4));
+        if (same) {
+            B[p2] = perm_b32(ra, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | (bb << 24));
+        } else {
+            B[p2] = perm_b32(rb, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | ((4u + bb) << 24));
+        }
+    }
+}
+
+template <int G>
+__global__ void __launch_bounds__(kThreads)
+tq_gemv_kernel(Params p) {
+    constexpr int NB = (G + 4) / 5;
+    constexpr int NQ = G / 8;             // MFMAs per group (8 trits per lane each)
+    __shared__ uint2 lut[256];
+    __shared__ int list[kMaxList];
+    __shared__ int list_n;
+    __shared__ float red[kWaves][4][64];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+
+    {   // byte -> five trits, as bf16 high bytes of 2t
+        int b = tid;
+        uint32_t lo = 0, hi = 0;
+        if (b < 243) {
+            int v = b;
+            uint32_t h[5];
+#pragma unroll
+            for (int q = 0; q < 5; ++q) { h[q] = trit_hi_byte(v % 3); v /= 3; }
+            lo = h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24);
+            hi = h[4];
+        }
+        lut[b] = make_uint2(lo, hi);
+    }
+
+    const int item = blockIdx.x;
+    const int rb = item % p.row_blocks;
+    const int e = item / p.row_blocks;
+
+    if (p.grouped) {
+        if (wave == 0) {
+            int count = 0;
+            const int total = p.M * p.top_k;
+            for (int base = 0; base < total; base += 64) {
+                int idx = base + lane;
+                bool pred = idx < total && p.ids[idx] == e;
+                uint64_t mask = __ballot(pred);
+                int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+                if (pred) list[pos] = idx;
+                count += __popcll(mask);
+            }
+            if (lane == 0) list_n = count;
+        }
+    }
+    __syncthreads();
+    const int n_list = p.grouped ? list_n : p.M;
+    if (n_list == 0) return;
+
+    const uint8_t* C0 = p.codes0 + (int64_t)e * p.code_stride;
+    const uint8_t* C1 = p.codes1 ? p.codes1 + (int64_t)e * p.code_stride : nullptr;
+    const uint16_t* S0 = p.scales0 + (int64_t)e * p.scale_stride;
+    const uint16_t* S1 = p.scales1 ? p.scales1 + (int64_t)e * p.scale_stride : nullptr;
+
+    const int col = lane & 15;
+    const int kb = lane >> 4;                 // group within a quad (B side)
+    const int64_t n = (int64_t)rb * 16 + col;
+    const bool row_ok = n < p.N;
+    const int ar = lane & 15;                 // A row: 4 * token + group
+    const int am = ar >> 2;
+    const bool a_diag = (ar & 3) == kb;
+    const int nquads = (p.ng + 3) >> 2;
+
+    for (int tok0 = 0; tok0 < n_list; tok0 += kChunk) {
+        const int ntok = min(kChunk, n_list - tok0);
+        const int ntq = (ntok + 3) >> 2;
+        float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+
+        for (int qd = wave; qd < nquads; qd += kWaves) {
+            const int g = 4 * qd + kb;
+            const bool g_ok = row_ok && g < p.ng;
+            float sc[2][4];
+#pragma unroll
+            for (int pl = 0; pl < 2; ++pl) {
+                const uint16_t* S = pl == 0 ? S0 : S1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int gi = 4 * qd + i;
+                    sc[pl][i] = (pl < p.planes && row_ok && gi < p.ng)
+                                    ? 0.5f * f16_bits_to_f32(S[n * p.ng + gi]) : 0.f;
+                }
+            }
+            for (int pl = 0; pl < p.planes; ++pl) {
+                uint32_t B[G / 2];
+                if (g_ok) {
+                    const uint8_t* Cp = pl == 0 ? C0 : C1;
+                    decode_group<G>(Cp + (n * p.ng + g) * NB, lut, B);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < G / 2; ++i) B[i] = 0u;
+                }
+                for (int tq = 0; tq < ntq; ++tq) {
+                    const int tl = 4 * tq + am;       // token slot of this A lane
+                    const bool a_ok = a_diag && tl < ntok && g < p.ng;
+                    int64_t xrow = 0;
+                    if (a_ok) {
+                        const int s = p.grouped ? list[tok0 + tl] : (tok0 + tl);
+                        xrow = p.grouped ? (int64_t)(s / p.top_k) : (int64_t)s;
+                    }
+                    const uint32_t* xp = (const uint32_t*)(p.x + xrow * p.K + (int64_t)g * G);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        u32x4 a = {0u, 0u, 0u, 0u};
+                        if (a_ok) {
+                            u32x4a v = *(const u32x4a*)(xp + 4 * q);
+                            a = u32x4{v.x, v.y, v.z, v.w};
+                        }
+                        u32x4 bq = {B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]};
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq), acc,
+                            0, 0, 0);
+                    }
+                    const float contrib = sc[pl][0] * acc[0] + sc[pl][1] * acc[1] +
+                                          sc[pl][2] * acc[2] + sc[pl][3] * acc[3];
+                    if (tq == 0) yacc[0] += contrib;
+                    else if (tq == 1) yacc[1] += contrib;
+                    else if (tq == 2) yacc[2] += contrib;
+                    else yacc[3] += contrib;
+                }
+            }
+        }
+
+        // wave partials -> LDS -> fixed-order sum in wave 0
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) red[wave][tq][lane] = yacc[tq];
+        __syncthreads();
+        if (wave == 0) {
+            for (int tq = 0; tq < ntq; ++tq) {
+                float v = red[0][tq][lane];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) v += red[w][tq][lane];
+                const int tl = 4 * tq + (lane >> 4);
+                if (tl < ntok && row_ok) {
+                    const int s = p.grouped ? list[tok0 + tl] : (tok0 + tl);
+                    const int64_t idx = (int64_t)s * p.N + n;
+                    if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
+                    else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Rows of y whose expert id is out of range become NaN.
+__global__ void bad_ids_kernel(const int32_t* ids, int total, int n_experts, int64_t N, void* y,
+                               int y_dtype) {
+    const int idx = blockIdx.x;
+    if (idx >= total) return;
+    const int e = ids[idx];
+    if (e >= 0 && e < n_experts) return;
+    for (int64_t n = threadIdx.x; n < N; n += blockDim.x) {
+        const int64_t o = (int64_t)idx * N + n;
+        if (y_dtype == TQ_F32) ((float*)y)[o] = __builtin_nanf("");
+        else ((uint16_t*)y)[o] = 0x7fc0u;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
+    Params p;
+    p.x = a.x;
+    p.K = a.K;
+    p.N = a.N;
+    p.ng = (int)(a.K / a.G);
+    p.codes0 = a.codes[0];
+    p.codes1 = a.planes == 2 ? a.codes[1] : nullptr;
+    p.scales0 = a.scales[0];
+    p.scales1 = a.planes == 2 ? a.scales[1] : nullptr;
+    p.planes = a.planes;
+    const int nb = (a.G + 4) / 5;
+    p.code_stride = a.N * (int64_t)p.ng * nb;
+    p.scale_stride = a.N * (int64_t)p.ng;
+    p.grouped = a.n_experts > 0;
+    p.ids = a.ids;
+    p.top_k = a.top_k;
+    p.M = (int)a.M;
+    p.row_blocks = (int)((a.N + 15) / 16);
+    p.y = a.y;
+    p.y_dtype = a.y_dtype;
+    const int experts = p.grouped ? a.n_experts : 1;
+    const int64_t items = (int64_t)p.row_blocks * experts;
+    if (items == 0) return hipSuccess;
+    if (p.grouped) {
+        const int total = (int)(a.M * a.top_k);
+        hipLaunchKernelGGL(bad_ids_kernel, dim3(total), dim3(256), 0, s, a.ids, total,
+                           a.n_experts, a.N, a.y, a.y_dtype);
+    }
+    if (a.G == 64)
+        hipLaunchKernelGGL(tq_gemv_kernel<64>, dim3((unsigned)items), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(tq_gemv_kernel<128>, dim3((unsigned)items), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+int tq_max_grouped_pairs() { return kMaxList; }
+
+}  // namespace dmm

@@ -1,0 +1,192 @@
+/*
+ * decode_matmul.h -- C ABI of the packed ternary-code matmul library for
+ * AMD MI355X (gfx950).
+ *
+ * Two weight formats, both decoded inside the matmul kernels (no bf16 copy of
+ * the weight matrix is ever written):
+ *
+ *  1. Mean-abs ternary ("Does your weight format deserve a kernel?",
+ *     pack-unpack-run, sections "Three values and a shared scale", "Five
+ *     trits in a byte", "Count the bytes you actually wrote"): a group of G
+ *     consecutive weights of a row shares s = fp16(mean |W|); each weight is
+ *     t = clip(round(W/s), -1, 1); five trits per byte, b = sum_q (t_q+1) 3^q,
+ *     first trit least significant; ceil(G/5) code bytes per group.
+ *     Optionally a second plane quantizes the residual of the first
+ *     (FUCINA README, "The method": W ~ d1 T1 + d2 T2).
+ *
+ *  2. Route B code book ("A Discrete Weight Language for Large Language
+ *     Models", sections 3.2, 3.3, 4.1, 4.2): one byte per weight indexes a
+ *     243-entry table of 5-step ternary ladder values, times one fp32 scale
+ *     per layer and an optional fp16 scale per output row.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named d_* or documented "device" are device pointers owned by
+ *    the caller; the library keeps no global state and allocates no memory.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued asynchronously on it; the return value is a host-side
+ *    tq_status, decided before anything is enqueued (argument errors never
+ *    launch a kernel).  TQ_ERR_HIP means a launch was rejected by the runtime.
+ *  - Data errors that only the device can see are OR-ed into the caller's
+ *    int32 *d_status as TQ_DATA_* flags.  The call first sets *d_status to 0
+ *    (with a kernel on `stream`, not a memset); read it after synchronizing.
+ *  - Matrices are dense and row-major.  The packed layout of a [rows, K]
+ *    matrix at group size G is planar:
+ *        codes  uint8  [rows][ceil(K/G)][ceil(G/5)]
+ *        scales fp16   [rows][ceil(K/G)]        (IEEE binary16 bit patterns)
+ *    A ragged final group (K % G != 0) has K - (ceil(K/G)-1) G members and
+ *    still occupies ceil(G/5) bytes; its unused trit slots are padding.
+ *  - bf16 values are passed as uint16 bit patterns.
+ *  - Calls that overlap on one stream are ordered; calls on different
+ *    streams that write the same buffers race, as usual.
+ */
+#ifndef DECODE_MATMUL_H
+#define DECODE_MATMUL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Host-side status codes (return values). */
+enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_NULL = 1,         /* a required pointer is NULL                     */
+    TQ_ERR_SHAPE = 2,        /* a size is negative, inconsistent or too large  */
+    TQ_ERR_UNSUPPORTED = 3,  /* G not in {64, 128}, planes not in {1, 2}, ...   */
+    TQ_ERR_DTYPE = 4,        /* unknown output dtype                           */
+    TQ_ERR_ALIGN = 5,        /* a pointer is not aligned as documented         */
+    TQ_ERR_HIP = 6           /* the HIP runtime rejected a launch              */
+};
+
+/* Device-side data-error flags, OR-ed into *d_status. */
+enum tq_data_flag {
+    TQ_DATA_RANGE = 1,       /* non-finite weight, or group scale overflows fp16 */
+    TQ_DATA_CODE = 2,        /* byte value 243..255 in a ternary package         */
+    TQ_DATA_PADDING = 4      /* a padding trit slot does not decode to zero      */
+};
+
+/* Element types of outputs. */
+enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 };
+
+/*
+ * tq_pack -- quantize and pack W (pack-unpack-run, "Three values and a
+ * shared scale" and "Five trits in a byte").
+ *
+ *  W        device fp32 [rows, K], row-major, 4-byte aligned.
+ *  G        group size, 64 or 128.
+ *  planes   1 or 2.  Plane 2 quantizes R = fl32(W - s1 t1) with the same
+ *           rule (FUCINA README, "The method").
+ *  codes1, scales1   device outputs of plane 1 (layout above); scales 2-byte
+ *           aligned; codes any alignment.
+ *  codes2, scales2   outputs of plane 2; must be NULL when planes == 1.
+ *  d_status device int32; receives TQ_DATA_RANGE if a weight is not finite or
+ *           a group mean rounds to fp16 infinity.  Such a group is written as
+ *           scale 0 and all-zero trits.
+ *
+ * Per group of n members: S = sum |W_j| in float64, j ascending; mean =
+ * S / n in float64; s = fp16 nearest-even of mean (one rounding);
+ * t_j = sign(W_j) if s > 0 and |W_j| > s/2, else 0 (the exact form of
+ * clip(round(W_j/s), -1, 1) with ties to even).  Bit-exact and
+ * deterministic.
+ */
+int tq_pack(const float* W, int64_t rows, int64_t K, int32_t G, int32_t planes,
+            uint8_t* codes1, uint16_t* scales1, uint8_t* codes2, uint16_t* scales2,
+            int32_t* d_status, void* stream);
+
+/*
+ * tq_unpack -- decode a package to weights (pack-unpack-run, "Five trits in
+ * a byte": the format rejects bytes 243..255 and padding must decode to 0).
+ *
+ *  codes, scales  device package of a [rows, K] matrix at group size G.
+ *  W_out          device [rows, K] of out_dtype: TQ_F32 gives s*t exactly,
+ *                 TQ_BF16 gives bf16 nearest-even of s*t.  4-byte aligned
+ *                 for fp32, 2-byte for bf16.
+ *  d_status       device int32; TQ_DATA_CODE / TQ_DATA_PADDING flags.  An
+ *                 invalid byte decodes as five zero trits.
+ */
+int tq_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t K,
+              int32_t G, void* W_out, int32_t out_dtype, int32_t* d_status, void* stream);
+
+/*
+ * tq_matmul -- y = x W_hat^T over a ternary package, decoded in-kernel
+ * (pack-unpack-run, "What survives the round trip?": the runtime decodes
+ * small pieces inside the matrix multiplication; FUCINA README, "Runtime
+ * requirements": second-plane outputs are summed with the first, and the
+ * expert matmul selects each token's experts).
+ *
+ *  x          device bf16 [M, K] (M tokens), 4-byte aligned.
+ *  codes1, scales1   plane 1.  Dense: one [N, K] package.  Grouped:
+ *             n_experts packages back to back, [n_experts][N][K/G][...].
+ *  codes2, scales2   optional plane 2 with the same layout (NULL = 1 plane);
+ *             W_hat = s1 T1 + s2 T2.
+ *  G          64 or 128; K % G must be 0.
+ *  n_experts  0 = dense: y is [M, N].  > 0 = grouped: expert_ids is device
+ *             int32 [M, top_k] and y is [M, top_k, N] with
+ *             y[t, j] = x[t] W_hat_{expert_ids[t, j]}^T.  A (t, j) whose id
+ *             is outside [0, n_experts) gets a row of NaN.
+ *  y          device output of y_dtype (fp32, or bf16 nearest-even of the
+ *             fp32 result).
+ *
+ * Accuracy: fp32 accumulation of exact trit-times-activation products, one
+ * fp32 multiply by the group scale per group; |y - y_ref| <= 2e-3 sum_k
+ * |x_k w_hat_k| against a float64 reference.  Bytes are not validated here
+ * (an invalid byte contributes an unspecified but finite value; memory
+ * accesses stay in bounds).  M = 0 or N = 0 is a no-op; with K = 0, x and
+ * the package may be NULL and y is written with zeros.
+ */
+int tq_matmul(const uint16_t* x, int64_t M, int64_t K,
+              const uint8_t* codes1, const uint16_t* scales1,
+              const uint8_t* codes2, const uint16_t* scales2,
+              int64_t N, int32_t G, int32_t n_experts, const int32_t* expert_ids,
+              int32_t top_k, void* y, int32_t y_dtype, void* stream);
+
+/*
+ * rb_table -- build the 243-entry Route B code book on the host (Route B
+ * paper, section 3.2: the 3^5 words of a 5-step ternary ladder are
+ * enumerated once per layer).
+ *
+ *  ladder     host fp32 [5], a_1..a_5.
+ *  table_out  host fp32 [243]; entry b is sum_i c_i a_i for the word
+ *             (c_1..c_5) whose base-3 encoding sum_i (c_i+1) 3^(5-i) is b
+ *             (c_1 most significant), summed in float64 for i = 1..5 and
+ *             rounded once to fp32.
+ *
+ * The per-layer scale alpha is not folded in; rb_matmul takes it separately.
+ */
+int rb_table(const float* ladder, float* table_out);
+
+/*
+ * rb_matmul -- Route B matmul (Route B paper, section 4.2: code bytes are
+ * dereferenced through the code book inside the GEMM; the per-row scale is
+ * applied to the output accumulator before the bias add):
+ *
+ *     y[m, n] = alpha * rho_n * sum_k x[m, k] * table[codes[n, k]]  (+ bias[n])
+ *
+ *  x          device bf16 [M, K] (fastest when 4-byte aligned with K even).
+ *  codes      device uint8 [N, K] (one code per weight), any alignment.
+ *  table      device fp32 [243] (e.g. from rb_table), 4-byte aligned.
+ *  alpha      per-layer fp32 scale.
+ *  row_scale  device fp16 [N] (rho_n) or NULL (rho = 1).
+ *  bias       device fp32 [N] or NULL.
+ *  y          device [M, N] of y_dtype.
+ *
+ * M <= 16 runs a GEMV kernel that keeps each weight as an exact split of the
+ * table value into two bf16 terms (error < 2^-16 per term); M > 16 runs an
+ * MFMA kernel that decodes tiles of bf16 table values into LDS (error <=
+ * 2^-9 per term).  Both accumulate in fp32.  Codes 243..255 read a zero
+ * table entry.  M = 0 or N = 0 is a no-op; with K = 0, x and codes may be
+ * NULL and y = bias (or 0).
+ */
+int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+              const float* table, float alpha, const uint16_t* row_scale,
+              const float* bias, void* y, int32_t y_dtype, void* stream);
+
+/* Human-readable name of a tq_status value. */
+const char* tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_MATMUL_H */

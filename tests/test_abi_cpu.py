@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every entry point of
+include/decode_matmul.h, rejects bad arguments before touching the device,
+and its host-side code-book builder matches the oracle bit for bit."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_matmul.h")
+
+dmm = pytest.importorskip("decode_matmul_amd")
+lib = dmm.raw()
+
+TQ_ERR_NULL, TQ_ERR_SHAPE, TQ_ERR_UNSUPPORTED, TQ_ERR_DTYPE, TQ_ERR_ALIGN = 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x10000)          # never dereferenced: every call below fails first
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(dmm.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(7):
+        assert lib.tq_status_string(s) and lib.tq_status_string(s) != b"unknown status"
+    assert lib.tq_status_string(99) == b"unknown status"
+
+
+def test_rb_table_matches_oracle():
+    """Host code book vs the oracle on the workload ladders, the integer
+    ladder (exact b - 121) and the balanced ladder S0."""
+    ladders = [workloads.routeb_gemv(seed=s, N=1, K=1, M=1)["ladder"] for s in range(6)]
+    ladders.append(np.array([81, 27, 9, 3, 1], np.float32))
+    ladders.append(np.array([1, 1 / 3, 1 / 9, 1 / 27, 1 / 81], np.float32))
+    ladders.append(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
+    for a in ladders:
+        got = dmm.rb_table(a)
+        ref = oracle.rb_table(a)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_rb_table_null():
+    assert lib.rb_table(None, FAKE) == TQ_ERR_NULL
+
+
+def test_pack_argument_errors():
+    f = lib.tq_pack
+    assert f(None, 4, 64, 64, 1, FAKE, FAKE, None, None, FAKE, None) == TQ_ERR_NULL
+    assert f(FAKE, 4, 64, 64, 1, FAKE, FAKE, None, None, None, None) == TQ_ERR_NULL
+    assert f(FAKE, -1, 64, 64, 1, FAKE, FAKE, None, None, FAKE, None) == TQ_ERR_SHAPE
+    assert f(FAKE, 4, 64, 32, 1, FAKE, FAKE, None, None, FAKE, None) == TQ_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 64, 64, 3, FAKE, FAKE, None, None, FAKE, None) == TQ_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 64, 64, 2, FAKE, FAKE, None, None, FAKE, None) == TQ_ERR_NULL
+    assert f(FAKE, 4, 64, 64, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == TQ_ERR_SHAPE
+    assert f(FAKE_ODD, 4, 64, 64, 1, FAKE, FAKE, None, None, FAKE, None) == TQ_ERR_ALIGN
+    assert f(FAKE, 4, 64, 64, 1, FAKE, FAKE_ODD, None, None, FAKE, None) == TQ_ERR_ALIGN
+
+
+def test_unpack_argument_errors():
+    f = lib.tq_unpack
+    assert f(None, FAKE, 4, 64, 64, FAKE, 0, FAKE, None) == TQ_ERR_NULL
+    assert f(FAKE, FAKE, 4, 64, 100, FAKE, 0, FAKE, None) == TQ_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 4, 64, 64, FAKE, 7, FAKE, None) == TQ_ERR_DTYPE
+    assert f(FAKE, FAKE, 4, -64, 64, FAKE, 0, FAKE, None) == TQ_ERR_SHAPE
+    assert f(FAKE, FAKE, 4, 64, 64, FAKE_ODD, 0, FAKE, None) == TQ_ERR_ALIGN
+
+
+def test_matmul_argument_errors():
+    f = lib.tq_matmul
+    ok = (FAKE, 1, 128, FAKE, FAKE, None, None, 16, 64, 0, None, 1, FAKE, 0, None)
+    bad = list(ok); bad[8] = 96
+    assert f(*bad) == TQ_ERR_UNSUPPORTED
+    bad = list(ok); bad[2] = 100                       # K % G != 0
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[13] = 5
+    assert f(*bad) == TQ_ERR_DTYPE
+    bad = list(ok); bad[5] = FAKE                      # codes2 without scales2
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[9] = 4                         # grouped without ids
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[9] = 4; bad[10] = FAKE; bad[11] = 0
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[9] = 4; bad[10] = FAKE; bad[1] = 1000; bad[11] = 8
+    assert f(*bad) == TQ_ERR_SHAPE                     # M * top_k above the list limit
+    bad = list(ok); bad[0] = FAKE_ODD
+    assert f(*bad) == TQ_ERR_ALIGN
+    bad = list(ok); bad[1] = 0                         # M = 0: no-op
+    assert f(*bad) == 0
+    bad = list(ok); bad[7] = 0                         # N = 0: no-op
+    assert f(*bad) == 0
+
+
+def test_rb_matmul_argument_errors():
+    f = lib.rb_matmul
+    ok = [FAKE, 4, 64, FAKE, 8, FAKE, ctypes.c_float(0.02), None, None, FAKE, 0, None]
+    bad = list(ok); bad[3] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[5] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[10] = 2
+    assert f(*bad) == TQ_ERR_DTYPE
+    bad = list(ok); bad[2] = -1
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[5] = FAKE_ODD
+    assert f(*bad) == TQ_ERR_ALIGN
+    bad = list(ok); bad[1] = 0
+    assert f(*bad) == 0
+
+
+def test_binding_refuses_wrong_tensors():
+    import torch
+    x = torch.zeros(1, 64, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        dmm.tq_matmul(x, torch.zeros(16 * 13, dtype=torch.uint8),
+                      torch.zeros(16, dtype=torch.float16), 16, 64,
+                      torch.zeros(1, 16, dtype=torch.float32))
+    xb = torch.zeros(1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dmm.tq_matmul(xb, torch.zeros(15 * 13, dtype=torch.uint8),
+                      torch.zeros(16, dtype=torch.float16), 16, 64,
+                      torch.zeros(1, 16, dtype=torch.float32))

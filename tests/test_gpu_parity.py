@@ -1,0 +1,477 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Pack and unpack must match bit for bit; matmuls must satisfy
+|y - y_ref| <= 2e-3 * sum_k |x_k w_hat_k| for every element (the acceptance
+bound of the packed-matmul workloads), with y_ref and the sum in float64.
+Inputs are the seeded synthetic workloads of workloads.py and small ragged
+shapes around them.  Each GPU step prints its case first.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dmm():
+    import decode_matmul_amd
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return decode_matmul_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits16(a):
+    return np.ascontiguousarray(a).view(np.int16)
+
+
+def gpu_pack(dmm, W, G, planes):
+    rows, K = W.shape
+    cs, ss = dmm.packed_shape(rows, K, G)
+    c1 = torch.empty(cs, dtype=torch.uint8, device=DEV)
+    s1 = torch.empty(ss, dtype=torch.int16, device=DEV)
+    c2 = s2 = None
+    if planes == 2:
+        c2 = torch.empty(cs, dtype=torch.uint8, device=DEV)
+        s2 = torch.empty(ss, dtype=torch.int16, device=DEV)
+    st = dmm.tq_pack(dev(W), G, planes, c1, s1, c2, s2)
+    out = [host(c1), host(s1).view(np.uint16)]
+    if planes == 2:
+        out += [host(c2), host(s2).view(np.uint16)]
+    return out, int(host(st)[0])
+
+
+def y_host(y):
+    a = host(y)
+    if y.dtype == torch.bfloat16:
+        return oracle.bf16_bits_to_f64(host(y.view(torch.int16)).view(np.uint16))
+    return a.astype(np.float64)
+
+
+def assert_bound(y, y_ref, B, what):
+    r = oracle.check_bound(y, y_ref, B)
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+# ------------------------------------------------------------------ pack
+
+PACK_CASES = [
+    ("ternary_small 256x256", lambda: workloads.ternary_small()["W"], 64, 1),
+    ("ragged 37x70 G64", lambda: (np.random.default_rng(1).standard_normal((37, 70)) * 0.02).astype(np.float32), 64, 1),
+    ("ragged 5x300 G128", lambda: (np.random.default_rng(2).standard_normal((5, 300)) * 0.02).astype(np.float32), 128, 1),
+    ("single group 3x64", lambda: (np.random.default_rng(3).standard_normal((3, 64))).astype(np.float32), 64, 1),
+    ("two-plane 64x320", lambda: (np.random.default_rng(4).standard_normal((64, 320)) * 0.02).astype(np.float32), 64, 2),
+    ("two-plane ragged 9x200 G128", lambda: (np.random.default_rng(5).standard_normal((9, 200)) * 3).astype(np.float32), 128, 2),
+]
+
+
+@pytest.mark.parametrize("name,make,G,planes", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_pack_bit_exact(dmm, name, make, G, planes):
+    W = make()
+    say(f"tq_pack {name} G={G} planes={planes}")
+    got, st = gpu_pack(dmm, W, G, planes)
+    assert st == 0
+    if planes == 1:
+        c, s = oracle.quantize_pack(W, G)
+        ref = [c, s]
+    else:
+        (c1, s1), (c2, s2) = oracle.two_plane(W, G)
+        ref = [c1, s1, c2, s2]
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
+def test_pack_special_groups(dmm):
+    """Ties, zeros, tiny means, the largest finite scale; then non-finite
+    weights and fp16 overflow raise TQ_DATA_RANGE on their group only."""
+    W = np.zeros((8, 128), np.float32)
+    W[0, :64] = [0.75] * 32 + [-0.25] * 32
+    W[1, :64] = 2.0 ** -26
+    W[2, :64] = 65519.0
+    W[3, 64:] = np.linspace(-1, 1, 64)
+    W[4, :] = 1e-30
+    W[5, 5] = -0.64
+    say("tq_pack special groups")
+    got, st = gpu_pack(dmm, W, 64, 2)
+    (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    assert st == 0
+    for g, r in zip(got, [c1, s1, c2, s2]):
+        assert np.array_equal(g, r)
+    for bad, val in (("nan", np.nan), ("inf", np.inf), ("overflow", 65520.0)):
+        W2 = W.copy()
+        if bad == "overflow":
+            W2[6, 64:] = val
+        else:
+            W2[6, 70] = val
+        say(f"tq_pack range error {bad}")
+        got, st = gpu_pack(dmm, W2, 64, 1)
+        assert st == dmm.TQ_DATA_RANGE
+        c, s = oracle.quantize_pack(np.where(np.arange(8)[:, None] == 6, 0, W2).astype(np.float32), 64)
+        keep = np.ones((8, 2), bool)
+        keep[6, 1] = False
+        assert np.array_equal(got[0][keep], c[keep]) and np.array_equal(got[1][keep], s[keep])
+        assert np.all(got[0][6, 1] == 121) and got[1][6, 1] == 0
+
+
+def test_pack_full_ternary_gemv(dmm):
+    """14336 x 4096 at G=64, bit-exact over every group."""
+    W = workloads.ternary_gemv()["W"]
+    say("tq_pack ternary_gemv 14336x4096")
+    got, st = gpu_pack(dmm, W, 64, 1)
+    c, s = oracle.quantize_pack(W, 64)
+    assert st == 0 and np.array_equal(got[0], c) and np.array_equal(got[1], s)
+
+
+def test_pack_full_moe_two_plane_sampled(dmm):
+    """All 64 experts (2 GiB of fp32) packed in one call; two planes checked
+    bit-exact on four sampled experts."""
+    d = workloads.moe_two_plane()
+    W = d["W"].reshape(-1, 4096)
+    say("tq_pack moe_two_plane 131072x4096 two planes")
+    got, st = gpu_pack(dmm, W, 64, 2)
+    assert st == 0
+    for e in (0, 17, 40, 63):
+        rows = slice(e * 2048, (e + 1) * 2048)
+        (c1, s1), (c2, s2) = oracle.two_plane(W[rows], 64)
+        for g, r in zip(got, [c1, s1, c2, s2]):
+            assert np.array_equal(g[rows], r)
+
+
+# ------------------------------------------------------------------ unpack
+
+@pytest.mark.parametrize("rows,K,G", [(256, 256, 64), (11, 70, 64), (7, 300, 128), (1, 64, 64)])
+def test_unpack_bit_exact(dmm, rows, K, G):
+    W = (np.random.default_rng(rows + K).standard_normal((rows, K)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, G)
+    ref = oracle.unpack(c, s, K, G)
+    for odt in (torch.float32, torch.bfloat16):
+        say(f"tq_unpack {rows}x{K} G={G} {odt}")
+        out = torch.empty((rows, K), dtype=odt, device=DEV)
+        st = dmm.tq_unpack(dev(c), dev(bits16(s)), rows, K, G, out)
+        assert int(host(st)[0]) == 0
+        if odt == torch.float32:
+            assert np.array_equal(host(out).view(np.uint32), ref.astype(np.float32).view(np.uint32))
+        else:
+            got = host(out.view(torch.int16)).view(np.uint16)
+            assert np.array_equal(got, oracle.f64_to_bf16_bits(ref))
+
+
+def test_unpack_rejects_bad_bytes(dmm):
+    W = (np.random.default_rng(9).standard_normal((4, 128)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    ref = oracle.unpack(c, s, 128, 64)
+    for bad, flag in ((243, 2), (255, 2)):
+        c2 = c.copy()
+        c2[2, 1, 4] = bad
+        out = torch.empty((4, 128), dtype=torch.float32, device=DEV)
+        say(f"tq_unpack invalid byte {bad}")
+        st = dmm.tq_unpack(dev(c2), dev(bits16(s)), 4, 128, 64, out)
+        assert int(host(st)[0]) == flag
+        got = host(out)
+        mask = np.ones((4, 128), bool)
+        mask[2, 64 + 20: 64 + 25] = False
+        assert np.array_equal(got[mask], ref[mask].astype(np.float32))
+        assert np.all(got[2, 84:89] == 0)
+    c3 = c.copy()
+    c3[1, 0, 12] += 81                   # padding digit of byte 12 -> 2
+    out = torch.empty((4, 128), dtype=torch.float32, device=DEV)
+    say("tq_unpack bad padding")
+    st = dmm.tq_unpack(dev(c3), dev(bits16(s)), 4, 128, 64, out)
+    assert int(host(st)[0]) == 4
+
+
+# ------------------------------------------------------------------ tq_matmul
+
+def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    if planes == 1:
+        c1, s1 = oracle.quantize_pack(W, G)
+        c2 = s2 = None
+    else:
+        (c1, s1), (c2, s2) = oracle.two_plane(W, G)
+    y_ref, B = oracle.matmul_ref(xb, oracle.ternary_weights(K, G, c1, s1, c2, s2))
+
+    def put_codes(c):
+        if c is None:
+            return None
+        flat = np.concatenate([np.zeros(code_off, np.uint8), c.reshape(-1)])
+        return dev(flat)[code_off:]
+
+    xs = np.concatenate([np.zeros(x_off, np.uint16), xb.reshape(-1)])
+    xd = dev(bits16(xs))[x_off:].view(M, K)
+    y = torch.empty((M, N), dtype=ydt, device=DEV)
+    say(f"tq_matmul M={M} N={N} K={K} G={G} planes={planes} y={ydt} off={code_off},{x_off}")
+    dmm.tq_matmul(xd, put_codes(c1), dev(bits16(s1)), N, G, y,
+                  put_codes(c2), None if s2 is None else dev(bits16(s2)))
+    return assert_bound(y_host(y), y_ref, B, f"tq M={M} N={N} K={K}")
+
+
+TQ_CASES = [
+    (1, 256, 256, 64, 1), (2, 100, 320, 64, 1), (3, 100, 320, 64, 1), (4, 100, 320, 64, 1),
+    (5, 100, 320, 64, 1), (8, 33, 192, 64, 1), (16, 64, 512, 64, 1), (17, 40, 256, 64, 1),
+    (33, 20, 128, 64, 1), (3, 48, 384, 128, 1), (4, 64, 256, 64, 2), (7, 30, 640, 128, 2),
+    (1, 1, 64, 64, 1), (1, 17, 64, 64, 2),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,planes", TQ_CASES)
+def test_tq_matmul_small(dmm, M, N, K, G, planes):
+    for ydt in (torch.float32, torch.bfloat16):
+        tq_case(dmm, M, N, K, G, planes, ydt, seed=M * 1000 + N + K)
+
+
+@pytest.mark.parametrize("code_off,x_off", [(1, 0), (2, 2), (3, 4), (5, 6)])
+def test_tq_matmul_offset_views(dmm, code_off, x_off):
+    """Non-zero view offsets of codes (any byte) and x (any 4-byte step)."""
+    tq_case(dmm, 3, 50, 320, 64, 2, torch.float32, seed=77, code_off=code_off, x_off=x_off)
+    tq_case(dmm, 1, 50, 256, 128, 1, torch.float32, seed=78, code_off=code_off, x_off=x_off)
+
+
+def test_tq_matmul_ternary_gemv_full(dmm):
+    """ternary_gemv: 14336 x 4096 at M = 1, 4, 16, codes packed on the GPU."""
+    d = workloads.ternary_gemv()
+    W, x = d["W"], d["x"]
+    (c, s), st = gpu_pack(dmm, W, 64, 1)
+    assert st == 0
+    w_hat = oracle.ternary_weights(4096, 64, c, s)
+    cd, sd = dev(c), dev(bits16(s))
+    for M in (1, 4, 16):
+        y_ref, B = oracle.matmul_ref(x[:M], w_hat)
+        for ydt in (torch.float32, torch.bfloat16):
+            y = torch.empty((M, 14336), dtype=ydt, device=DEV)
+            say(f"tq_matmul ternary_gemv M={M} {ydt}")
+            dmm.tq_matmul(dev(bits16(x[:M])), cd, sd, 14336, 64, y)
+            assert_bound(y_host(y), y_ref, B, f"ternary_gemv M={M}")
+
+
+def test_tq_matmul_ternary_small_full(dmm):
+    d = workloads.ternary_small()
+    (c, s), st = gpu_pack(dmm, d["W"], 64, 1)
+    y_ref, B = oracle.matmul_ref(d["x"], oracle.ternary_weights(256, 64, c, s))
+    y = torch.empty((1, 256), dtype=torch.float32, device=DEV)
+    say("tq_matmul ternary_small")
+    dmm.tq_matmul(dev(bits16(d["x"])), dev(c), dev(bits16(s)), 256, 64, y)
+    assert_bound(y_host(y), y_ref, B, "ternary_small")
+
+
+def grouped_case(dmm, E, N, K, T, top_k, planes, seed, bad_ids=False):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    xb = workloads.bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    if bad_ids:
+        ids[1, 0] = E
+        ids[2, top_k - 1] = -1
+    if planes == 2:
+        (c1, s1), (c2, s2) = oracle.two_plane(W.reshape(-1, K), 64)
+    else:
+        c1, s1 = oracle.quantize_pack(W.reshape(-1, K), 64)
+        c2 = s2 = None
+    y = torch.empty((T, top_k, N), dtype=torch.float32, device=DEV)
+    say(f"tq_matmul grouped E={E} N={N} K={K} T={T} top_k={top_k} planes={planes} bad={bad_ids}")
+    dmm.tq_matmul(dev(bits16(xb)), dev(c1), dev(bits16(s1)), N, 64, y,
+                  None if c2 is None else dev(c2), None if s2 is None else dev(bits16(s2)),
+                  n_experts=E, expert_ids=dev(ids), top_k=top_k)
+    got = y_host(y)
+
+    def w_of(e):
+        r = slice(e * N, (e + 1) * N)
+        return oracle.ternary_weights(K, 64, c1[r], s1[r],
+                                      None if c2 is None else c2[r], None if s2 is None else s2[r])
+    valid = (ids >= 0) & (ids < E)
+    ids_ok = np.where(valid, ids, 0)
+    y_ref, B = oracle.grouped_ref(xb, ids_ok, w_of)
+    assert_bound(got[valid], y_ref[valid], B[valid], "grouped")
+    assert np.all(np.isnan(got[~valid]))
+
+
+def test_tq_matmul_grouped_small(dmm):
+    grouped_case(dmm, 8, 40, 256, 6, 3, 2, seed=5)
+    grouped_case(dmm, 5, 33, 128, 9, 2, 1, seed=6)
+    grouped_case(dmm, 8, 40, 256, 6, 3, 2, seed=7, bad_ids=True)
+
+
+def test_tq_grouped_equals_dense_when_one_expert(dmm):
+    """Every (token, slot) routed to expert 2 gives, slot by slot, exactly the
+    dense result of expert 2's package (same kernel arithmetic)."""
+    rng = np.random.default_rng(12)
+    E, N, K, T = 4, 48, 256, 5
+    W = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    xb = workloads.bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    c, s = oracle.quantize_pack(W, 64)
+    ids = np.full((T, 2), 2, np.int32)
+    yg = torch.empty((T, 2, N), dtype=torch.float32, device=DEV)
+    yd = torch.empty((T, N), dtype=torch.float32, device=DEV)
+    say("tq_matmul grouped-vs-dense")
+    dmm.tq_matmul(dev(bits16(xb)), dev(c), dev(bits16(s)), N, 64, yg, n_experts=E,
+                  expert_ids=dev(ids), top_k=2)
+    r = slice(2 * N, 3 * N)
+    dmm.tq_matmul(dev(bits16(xb)), dev(c[r]), dev(bits16(s[r])), N, 64, yd)
+    g, d = host(yg), host(yd)
+    assert np.array_equal(g[:, 0], d) and np.array_equal(g[:, 1], d)
+
+
+def test_tq_matmul_moe_full_sampled(dmm):
+    """moe_two_plane: 64 experts of 2048 x 4096, 16 tokens, top-8, two planes
+    packed on the GPU; every (token, slot) of eight sampled experts checked."""
+    d = workloads.moe_two_plane()
+    W, x, ids = d["W"], d["x"], d["ids"]
+    (c1, s1, c2, s2), st = gpu_pack(dmm, W.reshape(-1, 4096), 64, 2)
+    assert st == 0
+    y = torch.empty((16, 8, 2048), dtype=torch.float32, device=DEV)
+    say("tq_matmul moe_two_plane full")
+    dmm.tq_matmul(dev(bits16(x)), dev(c1), dev(bits16(s1)), 2048, 64, y, dev(c2),
+                  dev(bits16(s2)), n_experts=64, expert_ids=dev(ids), top_k=8)
+    got = host(y)
+    experts = sorted(set(ids.reshape(-1).tolist()))
+    sample = experts[:: max(1, len(experts) // 8)][:8]
+    for e in sample:
+        r = slice(e * 2048, (e + 1) * 2048)
+        w = oracle.ternary_weights(4096, 64, c1[r], s1[r], c2[r], s2[r])
+        tt, jj = np.nonzero(ids == e)
+        y_ref, B = oracle.matmul_ref(x[tt], w)
+        assert_bound(got[tt, jj], y_ref, B, f"moe expert {e}")
+
+
+# ------------------------------------------------------------------ rb_matmul
+
+def rb_case(dmm, M, N, K, seed, ydt=torch.float32, rho=False, bias=False, code_off=0,
+            x_off=0, bad_codes=False, rows=None):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    if bad_codes:
+        codes[rng.integers(0, N, 20), rng.integers(0, K, 20)] = 250
+    ladder = np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32) * rng.uniform(0.8, 1.2)
+    table = oracle.rb_table(ladder.astype(np.float32))
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    rs = rng.uniform(0.5, 1.5, N).astype(np.float16).view(np.uint16) if rho else None
+    bs = rng.standard_normal(N).astype(np.float32) if bias else None
+    alpha = np.float32(0.02)
+    cflat = np.concatenate([np.zeros(code_off, np.uint8), codes.reshape(-1)])
+    cd = dev(cflat)[code_off:].view(N, K)
+    xs = np.concatenate([np.zeros(x_off, np.uint16), xb.reshape(-1)])
+    xd = dev(bits16(xs))[x_off:].view(M, K)
+    y = torch.empty((M, N), dtype=ydt, device=DEV)
+    say(f"rb_matmul M={M} N={N} K={K} y={ydt} rho={rho} bias={bias} off={code_off},{x_off}")
+    dmm.rb_matmul(xd, cd, dev(table), alpha, y, None if rs is None else dev(bits16(rs)),
+                  None if bs is None else dev(bs))
+    got = y_host(y)
+    sel = slice(None) if rows is None else rows
+    w = oracle.rb_weights(codes, table, alpha, rs)
+    y_ref, B = oracle.matmul_ref(xb[sel], w, bs)
+    return assert_bound(got[sel], y_ref, B, f"rb M={M} N={N} K={K}")
+
+
+RB_CASES = [
+    (1, 64, 64), (1, 100, 1000), (2, 37, 999), (3, 16, 128), (4, 256, 1024), (5, 100, 4096),
+    (8, 48, 200), (16, 80, 640), (1, 1, 1), (16, 17, 63),
+    (17, 130, 200), (64, 128, 128), (100, 256, 512), (300, 257, 333),
+]
+
+
+@pytest.mark.parametrize("M,N,K", RB_CASES)
+def test_rb_matmul_small(dmm, M, N, K):
+    rb_case(dmm, M, N, K, seed=M * 7 + N * 3 + K)
+    rb_case(dmm, M, N, K, seed=M + N + K, ydt=torch.bfloat16, rho=True, bias=True)
+
+
+@pytest.mark.parametrize("code_off,x_off", [(1, 1), (2, 0), (3, 3)])
+def test_rb_matmul_offsets_and_bad_codes(dmm, code_off, x_off):
+    rb_case(dmm, 4, 50, 256, 31, code_off=code_off, x_off=x_off, bad_codes=True)
+    rb_case(dmm, 40, 50, 256, 32, code_off=code_off, x_off=x_off, rho=True)
+
+
+def test_rb_matmul_routeb_gemv_full(dmm):
+    """routeb_gemv: N = K = 8192 at M = 1 and 4, fp32 and bf16 outputs."""
+    d = workloads.routeb_gemv()
+    table = dmm.rb_table(d["ladder"])
+    w = oracle.rb_weights(d["codes"], oracle.rb_table(d["ladder"]), d["alpha"])
+    cd, td = dev(d["codes"]), dev(table)
+    for M in (1, 4):
+        y_ref, B = oracle.matmul_ref(d["x"][:M], w)
+        for ydt in (torch.float32, torch.bfloat16):
+            y = torch.empty((M, 8192), dtype=ydt, device=DEV)
+            say(f"rb_matmul routeb_gemv M={M} {ydt}")
+            dmm.rb_matmul(dev(bits16(d["x"][:M])), cd, td, d["alpha"], y)
+            assert_bound(y_host(y), y_ref, B, f"routeb_gemv M={M}")
+
+
+def test_rb_matmul_routeb_prefill_full_sampled(dmm):
+    """routeb_prefill: M = 2048, K = N = 8192 with row scales; 96 sampled
+    token rows checked against the oracle over all 8192 outputs."""
+    d = workloads.routeb_prefill()
+    table = dmm.rb_table(d["ladder"])
+    y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=DEV)
+    say("rb_matmul routeb_prefill M=2048")
+    dmm.rb_matmul(dev(bits16(d["x"])), dev(d["codes"]), dev(table), d["alpha"], y,
+                  dev(bits16(d["row_scale"])))
+    got = y_host(y)
+    rows = np.sort(np.random.default_rng(0).choice(2048, 96, replace=False))
+    rows[0], rows[-1] = 0, 2047
+    w = oracle.rb_weights(d["codes"], oracle.rb_table(d["ladder"]), d["alpha"], d["row_scale"])
+    y_ref, B = oracle.matmul_ref(d["x"][rows], w)
+    assert_bound(got[rows], y_ref, B, "routeb_prefill")
+
+
+# ------------------------------------------------------------------ misc
+
+def test_zero_sizes_and_empty_k(dmm):
+    say("zero sizes")
+    y = torch.full((2, 3), 7.0, dtype=torch.float32, device=DEV)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    dmm.tq_matmul(x, torch.zeros(3 * 13, dtype=torch.uint8, device=DEV),
+                  torch.zeros(3, dtype=torch.int16, device=DEV), 3, 64,
+                  torch.empty((0, 3), dtype=torch.float32, device=DEV))
+    # K = 0: y = 0 (ternary) and y = bias (Route B)
+    x0 = torch.zeros((2, 0), dtype=torch.bfloat16, device=DEV)
+    dmm.tq_matmul(x0, torch.zeros(0, dtype=torch.uint8, device=DEV),
+                  torch.zeros(0, dtype=torch.int16, device=DEV), 3, 64, y)
+    assert np.all(host(y) == 0)
+    bias = torch.tensor([1.0, -2.0, 3.0], device=DEV)
+    tbl = torch.zeros(243, dtype=torch.float32, device=DEV)
+    dmm.rb_matmul(x0, torch.zeros((3, 0), dtype=torch.uint8, device=DEV), tbl, 0.5, y, None, bias)
+    assert np.array_equal(host(y), np.array([[1.0, -2.0, 3.0]] * 2, np.float32))
+
+
+def test_bit_determinism(dmm):
+    """Two runs of every matmul kernel give identical bits (fixed-order
+    reductions, no atomics on the accumulation path)."""
+    rng = np.random.default_rng(99)
+    W = (rng.standard_normal((300, 1024)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    xb = dev(bits16(workloads.bf16_bits(rng.standard_normal((40, 1024)).astype(np.float32))))
+    codes = dev(rng.integers(0, 243, (300, 1024), dtype=np.uint8))
+    tbl = dev(oracle.rb_table(np.array([1, .3, .1, .03, .01], np.float32)))
+    say("determinism")
+    outs = []
+    for _ in range(2):
+        y1 = torch.empty((4, 300), dtype=torch.float32, device=DEV)
+        dmm.tq_matmul(xb[:4], dev(c), dev(bits16(s)), 300, 64, y1)
+        y2 = torch.empty((4, 300), dtype=torch.float32, device=DEV)
+        dmm.rb_matmul(xb[:4], codes, tbl, 0.02, y2)
+        y3 = torch.empty((40, 300), dtype=torch.float32, device=DEV)
+        dmm.rb_matmul(xb, codes, tbl, 0.02, y3)
+        outs.append([host(t).view(np.uint32) for t in (y1, y2, y3)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
