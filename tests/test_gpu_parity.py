@@ -60,14 +60,17 @@ def gpu_pack(dmm, W, G, planes):
 
 
 def y_host(y):
-    a = host(y)
     if y.dtype == torch.bfloat16:
         return oracle.bf16_bits_to_f64(host(y.view(torch.int16)).view(np.uint16))
-    return a.astype(np.float64)
+    return host(y).astype(np.float64)
 
 
-def assert_bound(y, y_ref, B, what):
-    r = oracle.check_bound(y, y_ref, B)
+def stored_of(y):
+    return "bf16" if y.dtype == torch.bfloat16 else "f32"
+
+
+def assert_bound(y, y_ref, B, what, stored="f32"):
+    r = oracle.check_bound(y, y_ref, B, stored=stored)
     assert r["ok"], f"{what}: {r}"
     return r
 
@@ -224,7 +227,7 @@ def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0):
     say(f"tq_matmul M={M} N={N} K={K} G={G} planes={planes} y={ydt} off={code_off},{x_off}")
     dmm.tq_matmul(xd, put_codes(c1), dev(bits16(s1)), N, G, y,
                   put_codes(c2), None if s2 is None else dev(bits16(s2)))
-    return assert_bound(y_host(y), y_ref, B, f"tq M={M} N={N} K={K}")
+    return assert_bound(y_host(y), y_ref, B, f"tq M={M} N={N} K={K}", stored_of(y))
 
 
 TQ_CASES = [
@@ -262,7 +265,7 @@ def test_tq_matmul_ternary_gemv_full(dmm):
             y = torch.empty((M, 14336), dtype=ydt, device=DEV)
             say(f"tq_matmul ternary_gemv M={M} {ydt}")
             dmm.tq_matmul(dev(bits16(x[:M])), cd, sd, 14336, 64, y)
-            assert_bound(y_host(y), y_ref, B, f"ternary_gemv M={M}")
+            assert_bound(y_host(y), y_ref, B, f"ternary_gemv M={M}", stored_of(y))
 
 
 def test_tq_matmul_ternary_small_full(dmm):
@@ -380,7 +383,7 @@ def rb_case(dmm, M, N, K, seed, ydt=torch.float32, rho=False, bias=False, code_o
     sel = slice(None) if rows is None else rows
     w = oracle.rb_weights(codes, table, alpha, rs)
     y_ref, B = oracle.matmul_ref(xb[sel], w, bs)
-    return assert_bound(got[sel], y_ref, B, f"rb M={M} N={N} K={K}")
+    return assert_bound(got[sel], y_ref, B, f"rb M={M} N={N} K={K}", stored_of(y))
 
 
 RB_CASES = [
@@ -414,7 +417,7 @@ def test_rb_matmul_routeb_gemv_full(dmm):
             y = torch.empty((M, 8192), dtype=ydt, device=DEV)
             say(f"rb_matmul routeb_gemv M={M} {ydt}")
             dmm.rb_matmul(dev(bits16(d["x"][:M])), cd, td, d["alpha"], y)
-            assert_bound(y_host(y), y_ref, B, f"routeb_gemv M={M}")
+            assert_bound(y_host(y), y_ref, B, f"routeb_gemv M={M}", stored_of(y))
 
 
 def test_rb_matmul_routeb_prefill_full_sampled(dmm):
@@ -431,7 +434,7 @@ def test_rb_matmul_routeb_prefill_full_sampled(dmm):
     rows[0], rows[-1] = 0, 2047
     w = oracle.rb_weights(d["codes"], oracle.rb_table(d["ladder"]), d["alpha"], d["row_scale"])
     y_ref, B = oracle.matmul_ref(d["x"][rows], w)
-    assert_bound(got[rows], y_ref, B, "routeb_prefill")
+    assert_bound(got[rows], y_ref, B, "routeb_prefill", "bf16")
 
 
 # ------------------------------------------------------------------ misc

@@ -554,3 +554,14 @@ def test_check_bound_logic():
     assert not oracle.check_bound(yr + [0.0201, 0.0, 0.0], yr, B)["ok"]
     assert not oracle.check_bound(yr + [0.0, 1e-30, 0.0], yr, B)["ok"]
     assert not oracle.check_bound(np.array([np.nan, 0.0, -2.0]), yr, B)["ok"]
+
+
+def test_check_bound_bf16_allowance():
+    """bf16-stored results may also differ by half a bf16 spacing of y_ref:
+    2^-8 at 1.0 <= |y| < 2, 2^-9 at 0.5 <= |y| < 1."""
+    assert oracle.matmul.bf16_half_spacing(np.array([1.0, 1.99, 0.75]))[0] == 2.0 ** -8
+    assert oracle.matmul.bf16_half_spacing(np.array([0.75]))[0] == 2.0 ** -9
+    yr, B = np.array([1.5]), np.array([1.5])
+    assert oracle.check_bound(yr + 0.0035, yr, B, stored="bf16")["ok"]
+    assert not oracle.check_bound(yr + 0.0035, yr, B)["ok"]
+    assert not oracle.check_bound(yr + 0.0075, yr, B, stored="bf16")["ok"]
