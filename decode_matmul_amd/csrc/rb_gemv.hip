@@ -7,8 +7,10 @@
 // applied to the accumulator before the bias).
 //
 // Mapping onto gfx950:
-//  * The workgroup owns 16 output rows; its 8 waves split K into contiguous
-//    ranges and meet in LDS at the end (fixed summation order).
+//  * The workgroup (16 waves, one per CU: the replicated table fills LDS)
+//    owns 32 output rows; its waves split K into contiguous ranges, each
+//    wave streams both 16-row blocks with loads two steps ahead of the
+//    MFMAs, and the partials meet in LDS at the end (fixed summation order).
 //  * Each code byte is looked up in an LDS copy of the code book.  Every
 //    fp32 entry v is stored as two bf16 terms, hi = bf16(v) and
 //    lo = bf16(v - hi) (|v - hi - lo| <= 2^-17 |v|), packed as one dword.
@@ -27,8 +29,15 @@ namespace dmm {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 16;                // K split over the waves of a workgroup
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRB = 2;                    // 16-row blocks per workgroup, all streamed by each wave
+constexpr int kTileRows = 16 * kRB;       // tiled path: rows per workgroup
+constexpr int kTileK = 1024;              // tiled path: K bytes per tile (64 per wave)
+constexpr int kTilePitch = kTileK + 16;   // padded LDS row pitch: column reads hit distinct banks
+static_assert(kTileK == 64 * kWaves, "one 64-column slice per wave");
+static_assert(kTileRows == 2 * kWaves, "two rows fetched per wave");
+static_assert(kTileRows * kTilePitch >= kWaves * kRB * 64 * 4 * 4, "reduction fits the tile");
 constexpr int kLutBytes = 256 * 256;       // 256 entries x 64 copies x 4 B
 
 struct Params {
@@ -124,24 +133,32 @@ template <bool ALIGNED>
 __global__ void __launch_bounds__(kThreads)
 rb_gemv_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
-    __shared__ float red[kWaves * 64 * 4];
+    __shared__ float red[kWaves * kRB * 64 * 4];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
 
-    for (int i = tid; i < 256 * 64; i += kThreads) {
-        const int b = i >> 6;
-        const float v = b < 243 ? p.table[b] : 0.f;
-        *(uint32_t*)(lut + 4 * i) = split_entry(v);
+    {   // entry b, copies 16 (tid & 3) .. + 15: one global read per thread
+        const int b = tid >> 2;
+        const uint32_t e = split_entry(b < 243 ? p.table[b] : 0.f);
+        const u32x4 q = {e, e, e, e};
+        unsigned char* base = lut + b * 256 + (tid & 3) * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(base + 16 * i) = q;
     }
 
-    const int64_t rb = blockIdx.x;
     const int col = lane & 15;
     const int kb = lane >> 4;
-    const int64_t n = rb * 16 + col;
-    const bool row_ok = n < p.N;
-    const uint8_t* crow = p.codes + (row_ok ? n : 0) * p.K;
+    int64_t n[kRB];
+    bool row_ok[kRB];
+    const uint8_t* crow[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+        n[r] = ((int64_t)blockIdx.x * kRB + r) * 16 + col;
+        row_ok[r] = n[r] < p.N;
+        crow[r] = p.codes + (row_ok[r] ? n[r] : 0) * p.K;
+    }
     const int am = lane & 15;                                     // A row = token
     const bool a_ok = am < p.M;
     const uint16_t* xrow = p.x + (a_ok ? am : 0) * p.K;
@@ -154,61 +171,102 @@ rb_gemv_kernel(Params p) {
 
     __syncthreads();
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const uint32_t* D, const uint32_t* X) {
+    f32x4 acc[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    struct Slot {
+        uint32_t R[kRB][5];
+        uint32_t sh[kRB];
+        uint32_t X[8];
+    };
+
+    // codes of all kRB rows and 16 activations for one step.  Loads are issued
+    // unconditionally (rows past N read row 0, idle A lanes read token 0) and
+    // masked when consumed, so no branch separates a load from its wait.
+    auto stage = [&](int64_t st, Slot& S) {
+        const int64_t k = st * 64 + 16 * kb;
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) load_codes_raw<ALIGNED>(crow[r], k, S.R[r], S.sh[r]);
+        load_x16(xrow, k, p.K, false, S.X);
+    };
+
+    auto compute = [&](const uint32_t (*D)[4], const uint32_t* X) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            u32x4 bq, aq;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t addr = perm_b32(D[j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8));
-                bq[i] = *(const uint32_t*)(lut + addr);
-            }
+            u32x4 aq;
             const uint32_t x01 = X[2 * j], x23 = X[2 * j + 1];
             aq[0] = perm_b32(x01, x01, 0x01000100u);
             aq[1] = perm_b32(x01, x01, 0x03020302u);
             aq[2] = perm_b32(x23, x23, 0x01000100u);
             aq[3] = perm_b32(x23, x23, 0x03020302u);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aq),
-                                                          __builtin_bit_cast(bf16x8, bq), acc,
-                                                          0, 0, 0);
-        }
-    };
-    auto load_full = [&](int64_t st, uint32_t* R, uint32_t& sh, uint32_t* X) {
-        const int64_t k = st * 64 + 16 * kb;
-        if (row_ok) load_codes_raw<ALIGNED>(crow, k, R, sh);
-        else { R[0] = R[1] = R[2] = R[3] = R[4] = 0xffffffffu; sh = 0; }
-        if (a_ok) load_x16(xrow, k, p.K, false, X);
-        else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) X[i] = 0u;
+            for (int r = 0; r < kRB; ++r) {
+                u32x4 bq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t addr =
+                        perm_b32(D[r][j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8));
+                    bq[i] = *(const uint32_t*)(lut + addr);
+                }
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, aq), __builtin_bit_cast(bf16x8, bq), acc[r], 0,
+                    0, 0);
+            }
         }
     };
 
-    // steps entirely inside K, with the next step's loads in flight
+    auto compute_slot = [&](const Slot& S) {
+        uint32_t D[kRB][4], X[8];
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) {
+            realign16<ALIGNED>(S.R[r], S.sh[r], D[r]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) D[r][i] = row_ok[r] ? D[r][i] : 0xffffffffu;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) X[i] = a_ok ? S.X[i] : 0u;
+        compute(D, X);
+    };
+
+    // steps entirely inside K: loads run two steps ahead of the MFMAs
     const int64_t s_full_end = max(s_begin, min(s_end, p.full_steps));
     int64_t st = s_begin;
     if (st < s_full_end) {
-        uint32_t Rn[5], Xn[8], shn;
-        load_full(st, Rn, shn, Xn);
-        for (; st < s_full_end; ++st) {
-            uint32_t R[5], X[8], sh = shn;
-#pragma unroll
-            for (int i = 0; i < 5; ++i) R[i] = Rn[i];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) X[i] = Xn[i];
-            if (st + 1 < s_full_end) load_full(st + 1, Rn, shn, Xn);
-            uint32_t D[4];
-            realign16<ALIGNED>(R, sh, D);
-            compute(D, X);
+        // three register slots in rotation, no copies: while one step's MFMAs
+        // run, the next two steps' loads are in flight.  Prefetches past the
+        // end re-read the last full step and are never consumed.
+        const int64_t last = s_full_end - 1;
+        Slot s0, s1, s2;
+        stage(st, s0);
+        stage(min(st + 1, last), s1);
+        stage(min(st + 2, last), s2);
+        for (; st + 2 < s_full_end; st += 3) {
+            compute_slot(s0);
+            stage(min(st + 3, last), s0);
+            compute_slot(s1);
+            stage(min(st + 4, last), s1);
+            compute_slot(s2);
+            stage(min(st + 5, last), s2);
+        }
+        if (st < s_full_end) {
+            compute_slot(s0);
+            ++st;
+        }
+        if (st < s_full_end) {
+            compute_slot(s1);
+            ++st;
         }
     }
     // the ragged tail of K (and every step when rows are not 4-byte aligned)
     for (; st < s_end; ++st) {
         const int64_t k = st * 64 + 16 * kb;
-        uint32_t D[4], X[8];
-        if (row_ok) load_codes16_tail(crow, k, p.K, D);
-        else D[0] = D[1] = D[2] = D[3] = 0xffffffffu;
+        uint32_t D[kRB][4], X[8];
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) {
+            if (row_ok[r]) load_codes16_tail(crow[r], k, p.K, D[r]);
+            else D[r][0] = D[r][1] = D[r][2] = D[r][3] = 0xffffffffu;
+        }
         if (a_ok) load_x16(xrow, k, p.K, true, X);
         else {
 #pragma unroll
@@ -217,26 +275,177 @@ rb_gemv_kernel(Params p) {
         compute(D, X);
     }
 
-    // C[4*(lane>>4) + i][lane & 15]: token 4*(lane>>4)+i, row col
+    // C[4*(lane>>4) + i][lane & 15]: token 4*(lane>>4)+i, row col of block r
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
+    for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wave * kRB + r) * 64 + lane) * 4 + i] = acc[r][i];
     __syncthreads();
-    if (wave == 0 && row_ok) {
-        const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
-        const float bias = p.bias ? p.bias[n] : 0.f;
+    if (wave < kRB) {
+        const int r = wave;
+        if (row_ok[r]) {
+            const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n[r]]) : 1.f;
+            const float bias = p.bias ? p.bias[n[r]] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * kb + i;
-            if (m >= p.M) continue;
-            float v = red[lane * 4 + i];
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * kb + i;
+                if (m >= p.M) continue;
+                float v = red[(r * 64 + lane) * 4 + i];
+                for (int w = 1; w < kWaves; ++w) v += red[((w * kRB + r) * 64 + lane) * 4 + i];
+                v = v * rho;
+                v = v * p.alpha;
+                v = v + bias;
+                const int64_t idx = (int64_t)m * p.N + n[r];
+                if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
+                else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
+            }
+        }
+    }
+}
+
+// Fast path: codes 16-byte aligned, K % 1024 == 0, x 4-byte aligned.
+//
+// The workgroup (16 waves) owns 32 rows.  K is walked in tiles of 32 rows x
+// 1 KB: each wave fetches two rows of the tile with one 1 KB load per row
+// (every load instruction covers 1 KB of one row, the pattern HBM streams
+// best), two tiles ahead in registers; the tile is written to LDS and each
+// wave then reads its 64-column slice of all 32 rows in the MFMA layout.
+__global__ void __launch_bounds__(kThreads)
+rb_gemv_tiled_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char tile[kTileRows * kTilePitch];
+
+    const int tid = threadIdx.x;
+    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
+    const int lane = tid & 63;
+    const int64_t row0 = (int64_t)blockIdx.x * kTileRows;
+    const int64_t ntiles = p.K / kTileK;          // >= 1: the launcher requires K >= kTileK
+
+    // rows this wave fetches: 2 * wave, 2 * wave + 1 (clamped into range)
+    const uint8_t* grow[2];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) v += red[(w * 64 + lane) * 4 + i];
-            v = v * rho;
-            v = v * p.alpha;
-            v = v + bias;
-            const int64_t idx = (int64_t)m * p.N + n;
-            if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
-            else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
+    for (int i = 0; i < 2; ++i) {
+        const int64_t r = min(row0 + 2 * wave + i, p.N - 1);
+        grow[i] = p.codes + r * p.K + 16 * lane;
+    }
+    // activations of this wave's slice: token (lane & 15), 16 columns
+    const int am = lane & 15;
+    const bool a_ok = am < p.M;
+    const int col = lane & 15;
+    const int kb = lane >> 4;
+    const uint16_t* xrow = p.x + (a_ok ? am : 0) * p.K + 64 * wave + 16 * kb;
+
+    struct Stage {
+        u32x4a c[2];
+        uint32_t X[8];
+    };
+    auto fetch = [&](int64_t t, Stage& S) {
+        const int64_t tc = min(t, ntiles - 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) S.c[i] = *(const u32x4a*)(grow[i] + tc * kTileK);
+        const u32x4a* xp = (const u32x4a*)(xrow + tc * kTileK);
+        u32x4a a = xp[0], b = xp[1];
+        S.X[0] = a.x; S.X[1] = a.y; S.X[2] = a.z; S.X[3] = a.w;
+        S.X[4] = b.x; S.X[5] = b.y; S.X[6] = b.z; S.X[7] = b.w;
+    };
+
+    // the code-book read goes first so that waiting for it leaves the tile
+    // loads in flight (memory counters complete in order)
+    const int lb = tid >> 2;
+    const float tv = p.table[lb < 243 ? lb : 0];
+    Stage s0, s1;
+    fetch(0, s0);
+    fetch(1, s1);
+
+    {   // entry b, copies 16 (tid & 3) .. + 15
+        const int b = lb;
+        const uint32_t e = split_entry(b < 243 ? tv : 0.f);
+        const u32x4 q = {e, e, e, e};
+        unsigned char* base = lut + b * 256 + (tid & 3) * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(base + 16 * i) = q;
+    }
+
+    f32x4 acc[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t lane_off = (uint32_t)lane << 2;
+
+    auto step = [&](const Stage& S) {
+        __syncthreads();                                  // tile free again
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            *(u32x4*)(tile + (2 * wave + i) * kTilePitch + 16 * lane) =
+                u32x4{S.c[i].x, S.c[i].y, S.c[i].z, S.c[i].w};
+        __syncthreads();
+        uint32_t D[kRB][4];
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) {
+            u32x4 v = *(const u32x4*)(tile + (16 * r + col) * kTilePitch + 64 * wave + 16 * kb);
+            D[r][0] = v.x; D[r][1] = v.y; D[r][2] = v.z; D[r][3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 aq;
+            // lanes of tokens >= M hold token 0's activations: they only feed
+            // rows of C that are never stored
+            const uint32_t x01 = S.X[2 * j], x23 = S.X[2 * j + 1];
+            aq[0] = perm_b32(x01, x01, 0x01000100u);
+            aq[1] = perm_b32(x01, x01, 0x03020302u);
+            aq[2] = perm_b32(x23, x23, 0x01000100u);
+            aq[3] = perm_b32(x23, x23, 0x03020302u);
+#pragma unroll
+            for (int r = 0; r < kRB; ++r) {
+                u32x4 bq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t addr =
+                        perm_b32(D[r][j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8));
+                    bq[i] = *(const uint32_t*)(lut + addr);
+                }
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, aq), __builtin_bit_cast(bf16x8, bq), acc[r], 0,
+                    0, 0);
+            }
+        }
+    };
+
+    int64_t t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(s0);
+        fetch(t + 2, s0);
+        step(s1);
+        fetch(t + 3, s1);
+    }
+    if (t < ntiles) step(s0);
+
+    // partials of the 16 waves meet in the (now idle) tile buffer
+    __syncthreads();
+    float* red = (float*)tile;                                    // [kWaves][kRB][64][4]
+#pragma unroll
+    for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wave * kRB + r) * 64 + lane) * 4 + i] = acc[r][i];
+    __syncthreads();
+    if (wave < kRB) {
+        const int r = wave;
+        const int64_t n = row0 + 16 * r + col;
+        if (n < p.N) {
+            const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
+            const float bias = p.bias ? p.bias[n] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * kb + i;
+                if (m >= p.M) continue;
+                float v = red[(r * 64 + lane) * 4 + i];
+                for (int w = 1; w < kWaves; ++w) v += red[((w * kRB + r) * 64 + lane) * 4 + i];
+                v = v * rho;
+                v = v * p.alpha;
+                v = v + bias;
+                const int64_t idx = (int64_t)m * p.N + n;
+                if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
+                else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
+            }
         }
     }
 }
@@ -262,8 +471,16 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
     // vector activation loads need 4-byte aligned rows; otherwise every step
     // takes the element-wise path
     if ((a.K & 1) || ((uintptr_t)a.x & 3)) p.full_steps = 0;
-    const int64_t blocks = (a.N + 15) / 16;
+    const int64_t blocks = (a.N + 16 * kRB - 1) / (16 * kRB);
     if (blocks == 0 || a.M == 0) return hipSuccess;
+    // tiles need at least one full tile: K = 0 (null operands) takes the
+    // general path, which issues no loads at all
+    const bool tiled = a.K >= kTileK && (a.K % kTileK == 0) &&
+                       (((uintptr_t)a.codes & 15) == 0) && (((uintptr_t)a.x & 3) == 0);
+    if (tiled) {
+        hipLaunchKernelGGL(rb_gemv_tiled_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+        return hipGetLastError();
+    }
     const bool aligned4 = (((uintptr_t)a.codes & 3) == 0) && (a.K % 4 == 0);
     if (aligned4)
         hipLaunchKernelGGL(rb_gemv_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);

@@ -46,7 +46,7 @@ rb_prefill_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDT];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
 

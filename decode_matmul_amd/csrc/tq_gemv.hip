@@ -54,6 +54,7 @@ struct Params {
     int row_blocks;
     void* y;
     int y_dtype;
+    int list_bytes;                  // dynamic LDS for the grouped token list
 };
 
 // bf16 high byte of 2t for digit d = t + 1.
@@ -61,38 +62,46 @@ __device__ __forceinline__ uint32_t trit_hi_byte(int d) {
     return d == 2 ? 0x40u : (d == 0 ? 0xC0u : 0x00u);
 }
 
-// Load the NB code bytes of one group starting at byte address p into
-// dwords D[0..ceil(NB/4)-1] (byte i of the group = byte i%4 of D[i/4]).
-// Only dwords that hold at least one byte of the group are read.
+// Raw aligned words holding the NB code bytes of one group at byte address
+// p: W[0..NW-1] plus the byte shift sh = p & 3.  Every word read holds at
+// least one byte of the group (so no read leaves the package).
 template <int NB>
-__device__ __forceinline__ void load_group_bytes(const uint8_t* p, uint32_t* D) {
-    constexpr int ND = (NB + 3) / 4;
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
-    const uint32_t* aw = (const uint32_t*)(p - sh);      // keeps the global address space
-    uint32_t W[ND + 1];
+struct RawGroup {
+    static constexpr int NW = (NB == 13) ? 4 : 8;
+    uint32_t W[NW];
+    uint32_t sh;
+};
+
+template <int NB>
+__device__ __forceinline__ void load_group_raw(const uint8_t* p, RawGroup<NB>& R) {
+    R.sh = (uint32_t)((uintptr_t)p & 3);
+    const uint32_t* aw = (const uint32_t*)(p - R.sh);    // keeps the global address space
     if constexpr (NB == 13) {
-        // 13 bytes at offset sh <= 3 always fit the 16 aligned bytes.
+        // 13 bytes at offset sh <= 3 always fit the 16 aligned bytes
         u32x4a v = *(const u32x4a*)aw;
-        W[0] = v.x; W[1] = v.y; W[2] = v.z; W[3] = v.w; W[4] = 0;
+        R.W[0] = v.x; R.W[1] = v.y; R.W[2] = v.z; R.W[3] = v.w;
     } else {
         static_assert(NB == 26, "G = 64 or 128");
         u32x4a v = *(const u32x4a*)aw;
         u32x3a u = *(const u32x3a*)(aw + 4);
-        W[0] = v.x; W[1] = v.y; W[2] = v.z; W[3] = v.w;
-        W[4] = u.x; W[5] = u.y; W[6] = u.z;
-        W[7] = (sh == 3) ? aw[7] : 0u;     // byte 25 sits in dword 7 only if sh == 3
+        R.W[0] = v.x; R.W[1] = v.y; R.W[2] = v.z; R.W[3] = v.w;
+        R.W[4] = u.x; R.W[5] = u.y; R.W[6] = u.z;
+        R.W[7] = aw[R.sh == 3 ? 7 : 6];     // byte 25 sits in word 7 only if sh == 3
     }
-#pragma unroll
-    for (int i = 0; i < ND; ++i) D[i] = align_bytes(W[i + 1], W[i], sh);
 }
 
 // Decode one group (G trits) into G/2 bf16 pair registers, natural order.
 template <int G>
-__device__ __forceinline__ void decode_group(const uint8_t* p, const uint2* lut, uint32_t* B) {
+__device__ __forceinline__ void decode_group(const RawGroup<(G + 4) / 5>& R, const uint2* lut,
+                                             uint32_t* B) {
     constexpr int NB = (G + 4) / 5;
     constexpr int ND = (NB + 3) / 4;
     uint32_t D[ND];
-    load_group_bytes<NB>(p, D);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+        const uint32_t hi = (i + 1 < RawGroup<NB>::NW) ? R.W[i + 1] : 0u;
+        D[i] = align_bytes(hi, R.W[i], R.sh);
+    }
     uint32_t Elo[NB], Ehi[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -117,18 +126,24 @@ __device__ __forceinline__ void decode_group(const uint8_t* p, const uint2* lut,
     }
 }
 
-template <int G>
-__global__ void __launch_bounds__(kThreads)
+// G: group size.  PL: planes (1 or 2).  XLDS: the chunk's activations (<= 4
+// tokens) are staged in LDS; otherwise A operands are read from global memory
+// in chunks of 16 tokens.  SV: the four scales of a quad are one 8-byte load.
+template <int G, int PL, bool XLDS, bool SV>
+__global__ void __launch_bounds__(kThreads, (PL == 2 || G == 128) ? 2 : 3)
 tq_gemv_kernel(Params p) {
     constexpr int NB = (G + 4) / 5;
     constexpr int NQ = G / 8;             // MFMAs per group (8 trits per lane each)
+    constexpr int kTokChunk = XLDS ? 4 : kChunk;
     __shared__ uint2 lut[256];
-    __shared__ int list[kMaxList];
     __shared__ int list_n;
     __shared__ float red[kWaves][4][64];
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+    int* list = (int*)dyn;                                       // grouped: M * top_k
+    uint16_t* xs = (uint16_t*)(dyn + p.list_bytes);              // XLDS: [4][K]
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
 
     {   // byte -> five trits, as bf16 high bytes of 2t
@@ -149,97 +164,167 @@ tq_gemv_kernel(Params p) {
     const int rb = item % p.row_blocks;
     const int e = item / p.row_blocks;
 
-    if (p.grouped) {
-        if (wave == 0) {
-            int count = 0;
-            const int total = p.M * p.top_k;
-            for (int base = 0; base < total; base += 64) {
-                int idx = base + lane;
-                bool pred = idx < total && p.ids[idx] == e;
-                uint64_t mask = __ballot(pred);
-                int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
-                if (pred) list[pos] = idx;
-                count += __popcll(mask);
-            }
-            if (lane == 0) list_n = count;
+    if (p.grouped && wave == 0) {
+        int count = 0;
+        const int total = p.M * p.top_k;
+        for (int base = 0; base < total; base += 64) {
+            int idx = base + lane;
+            bool pred = idx < total && p.ids[idx] == e;
+            uint64_t mask = __ballot(pred);
+            int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+            if (pred) list[pos] = idx;
+            count += __popcll(mask);
         }
+        if (lane == 0) list_n = count;
     }
     __syncthreads();
     const int n_list = p.grouped ? list_n : p.M;
     if (n_list == 0) return;
 
-    const uint8_t* C0 = p.codes0 + (int64_t)e * p.code_stride;
-    const uint8_t* C1 = p.codes1 ? p.codes1 + (int64_t)e * p.code_stride : nullptr;
-    const uint16_t* S0 = p.scales0 + (int64_t)e * p.scale_stride;
-    const uint16_t* S1 = p.scales1 ? p.scales1 + (int64_t)e * p.scale_stride : nullptr;
+    const uint8_t* Cp[2];
+    const uint16_t* Sp[2];
+    Cp[0] = p.codes0 + (int64_t)e * p.code_stride;
+    Sp[0] = p.scales0 + (int64_t)e * p.scale_stride;
+    Cp[1] = PL == 2 ? p.codes1 + (int64_t)e * p.code_stride : Cp[0];
+    Sp[1] = PL == 2 ? p.scales1 + (int64_t)e * p.scale_stride : Sp[0];
 
     const int col = lane & 15;
     const int kb = lane >> 4;                 // group within a quad (B side)
     const int64_t n = (int64_t)rb * 16 + col;
     const bool row_ok = n < p.N;
+    const int64_t nc = row_ok ? n : 0;        // clamped row for branch-free loads
     const int ar = lane & 15;                 // A row: 4 * token + group
     const int am = ar >> 2;
     const bool a_diag = (ar & 3) == kb;
     const int nquads = (p.ng + 3) >> 2;
+    // this wave's quads: wave, wave + kWaves, ...
+    const int nmy = wave < nquads ? (nquads - wave + kWaves - 1) / kWaves : 0;
 
-    for (int tok0 = 0; tok0 < n_list; tok0 += kChunk) {
-        const int ntok = min(kChunk, n_list - tok0);
+    struct Slot {
+        RawGroup<NB> raw[PL];
+        uint32_t scw[PL][2];
+    };
+    // loads of the j-th quad of this wave, clamped so they never branch
+    auto stage = [&](int j, Slot& S) {
+        const int qd = wave + kWaves * min(j, nmy - 1);
+        const int g = 4 * qd + kb;
+        const int64_t gi = nc * p.ng + (g < p.ng ? g : 0);
+#pragma unroll
+        for (int pl = 0; pl < PL; ++pl) {
+            load_group_raw<NB>(Cp[pl] + gi * NB, S.raw[pl]);
+            if constexpr (SV) {
+                const uint32_t* sp = (const uint32_t*)(Sp[pl] + nc * p.ng + 4 * qd);
+                S.scw[pl][0] = sp[0];
+                S.scw[pl][1] = sp[1];
+            } else {
+                uint32_t h[4];
+#pragma unroll
+                for (int j2 = 0; j2 < 4; ++j2) {
+                    const int gj = 4 * qd + j2;
+                    h[j2] = Sp[pl][nc * p.ng + (gj < p.ng ? gj : 0)];
+                }
+                S.scw[pl][0] = h[0] | (h[1] << 16);
+                S.scw[pl][1] = h[2] | (h[3] << 16);
+            }
+        }
+    };
+
+    for (int tok0 = 0; tok0 < n_list; tok0 += kTokChunk) {
+        const int ntok = min(kTokChunk, n_list - tok0);
         const int ntq = (ntok + 3) >> 2;
+
+        if constexpr (XLDS) {
+            // stage x rows of this chunk: xs[t][0:K], zero rows past ntok
+            const int per_row = (int)(p.K >> 3);               // 16-byte pieces per row
+            for (int i = tid; i < 4 * per_row; i += kThreads) {
+                const int t = i / per_row, c = i - t * per_row;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (t < ntok) {
+                    const int sl = p.grouped ? list[tok0 + t] : (tok0 + t);
+                    const int64_t row = p.grouped ? (int64_t)(sl / p.top_k) : (int64_t)sl;
+                    u32x4a w = *(const u32x4a*)(p.x + row * p.K + 8 * c);
+                    v = u32x4{w.x, w.y, w.z, w.w};
+                }
+                *(u32x4*)(xs + t * p.K + 8 * c) = v;
+            }
+            __syncthreads();
+        }
+
         float yacc[4] = {0.f, 0.f, 0.f, 0.f};
 
-        for (int qd = wave; qd < nquads; qd += kWaves) {
+        // decode + MFMA of the j-th quad of this wave from its loaded slot
+        auto proc = [&](int j, const Slot& S) {
+            const int qd = wave + kWaves * j;
             const int g = 4 * qd + kb;
             const bool g_ok = row_ok && g < p.ng;
-            float sc[2][4];
 #pragma unroll
-            for (int pl = 0; pl < 2; ++pl) {
-                const uint16_t* S = pl == 0 ? S0 : S1;
+            for (int pl = 0; pl < PL; ++pl) {
+                float sc[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int gi = 4 * qd + i;
-                    sc[pl][i] = (pl < p.planes && row_ok && gi < p.ng)
-                                    ? 0.5f * f16_bits_to_f32(S[n * p.ng + gi]) : 0.f;
+                for (int j2 = 0; j2 < 4; ++j2) {
+                    const uint32_t w = S.scw[pl][j2 >> 1];
+                    const uint16_t h = (uint16_t)((j2 & 1) ? (w >> 16) : (w & 0xffffu));
+                    sc[j2] = (row_ok && 4 * qd + j2 < p.ng) ? 0.5f * f16_bits_to_f32(h) : 0.f;
                 }
-            }
-            for (int pl = 0; pl < p.planes; ++pl) {
                 uint32_t B[G / 2];
-                if (g_ok) {
-                    const uint8_t* Cp = pl == 0 ? C0 : C1;
-                    decode_group<G>(Cp + (n * p.ng + g) * NB, lut, B);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < G / 2; ++i) B[i] = 0u;
-                }
-                for (int tq = 0; tq < ntq; ++tq) {
-                    const int tl = 4 * tq + am;       // token slot of this A lane
+                decode_group<G>(S.raw[pl], lut, B);
+                const int ntq_eff = XLDS ? 1 : ntq;
+                for (int tq = 0; tq < ntq_eff; ++tq) {
+                    const int tl = 4 * tq + am;
                     const bool a_ok = a_diag && tl < ntok && g < p.ng;
                     int64_t xrow = 0;
-                    if (a_ok) {
-                        const int s = p.grouped ? list[tok0 + tl] : (tok0 + tl);
-                        xrow = p.grouped ? (int64_t)(s / p.top_k) : (int64_t)s;
+                    if (!XLDS && a_ok) {
+                        const int sl = p.grouped ? list[tok0 + tl] : (tok0 + tl);
+                        xrow = p.grouped ? (int64_t)(sl / p.top_k) : (int64_t)sl;
                     }
-                    const uint32_t* xp = (const uint32_t*)(p.x + xrow * p.K + (int64_t)g * G);
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
-                        u32x4 a = {0u, 0u, 0u, 0u};
+                        u32x4 A = {0u, 0u, 0u, 0u};
                         if (a_ok) {
-                            u32x4a v = *(const u32x4a*)(xp + 4 * q);
-                            a = u32x4{v.x, v.y, v.z, v.w};
+                            if constexpr (XLDS) {
+                                A = *(const u32x4*)(xs + tl * p.K + (int64_t)g * G + 8 * q);
+                            } else {
+                                u32x4a v = *(const u32x4a*)(p.x + xrow * p.K + (int64_t)g * G +
+                                                            8 * q);
+                                A = u32x4{v.x, v.y, v.z, v.w};
+                            }
                         }
                         u32x4 bq = {B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) bq[i] = g_ok ? bq[i] : 0u;
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq), acc,
+                            __builtin_bit_cast(bf16x8, A), __builtin_bit_cast(bf16x8, bq), acc,
                             0, 0, 0);
                     }
-                    const float contrib = sc[pl][0] * acc[0] + sc[pl][1] * acc[1] +
-                                          sc[pl][2] * acc[2] + sc[pl][3] * acc[3];
+                    const float contrib =
+                        sc[0] * acc[0] + sc[1] * acc[1] + sc[2] * acc[2] + sc[3] * acc[3];
                     if (tq == 0) yacc[0] += contrib;
                     else if (tq == 1) yacc[1] += contrib;
                     else if (tq == 2) yacc[2] += contrib;
                     else yacc[3] += contrib;
                 }
             }
+        };
+
+        if (nmy > 0) {
+            // three slots in rotation: two quads' loads stay in flight while
+            // one quad is decoded and multiplied
+            Slot s0, s1, s2;
+            stage(0, s0);
+            stage(1, s1);
+            stage(2, s2);
+            int j = 0;
+            for (; j + 2 < nmy; j += 3) {
+                proc(j, s0);
+                stage(j + 3, s0);
+                proc(j + 1, s1);
+                stage(j + 4, s1);
+                proc(j + 2, s2);
+                stage(j + 5, s2);
+            }
+            if (j < nmy) proc(j, s0);
+            if (j + 1 < nmy) proc(j + 1, s1);
         }
 
         // wave partials -> LDS -> fixed-order sum in wave 0
@@ -253,8 +338,8 @@ tq_gemv_kernel(Params p) {
                 for (int w = 1; w < kWaves; ++w) v += red[w][tq][lane];
                 const int tl = 4 * tq + (lane >> 4);
                 if (tl < ntok && row_ok) {
-                    const int s = p.grouped ? list[tok0 + tl] : (tok0 + tl);
-                    const int64_t idx = (int64_t)s * p.N + n;
+                    const int sl = p.grouped ? list[tok0 + tl] : (tok0 + tl);
+                    const int64_t idx = (int64_t)sl * p.N + n;
                     if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
                     else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
                 }
@@ -309,10 +394,30 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(bad_ids_kernel, dim3(total), dim3(256), 0, s, a.ids, total,
                            a.n_experts, a.N, a.y, a.y_dtype);
     }
-    if (a.G == 64)
-        hipLaunchKernelGGL(tq_gemv_kernel<64>, dim3((unsigned)items), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(tq_gemv_kernel<128>, dim3((unsigned)items), dim3(kThreads), 0, s, p);
+    // activations staged in LDS when a chunk of <= 4 tokens fits comfortably
+    const int64_t xlds_bytes = 4 * a.K * 2;
+    // dense: M tokens per workgroup; grouped: on average M * top_k / experts
+    const int64_t tok_per_item =
+        p.grouped ? ((int64_t)a.M * a.top_k + a.n_experts - 1) / a.n_experts : a.M;
+    const bool xlds = tok_per_item <= 4 && xlds_bytes <= 64 * 1024;
+    p.list_bytes = p.grouped ? (int)(((int64_t)a.M * a.top_k * 4 + 15) & ~15) : 0;
+    const size_t smem = (size_t)p.list_bytes + (xlds ? (size_t)xlds_bytes : 0);
+    const bool sv = (p.ng % 4 == 0) && (((uintptr_t)a.scales[0] & 7) == 0) &&
+                    (a.planes < 2 || (((uintptr_t)a.scales[1] & 7) == 0));
+    const dim3 grid((unsigned)items), block(kThreads);
+#define DMM_TQ_LAUNCH(G_, P_, X_, S_) \
+    hipLaunchKernelGGL((tq_gemv_kernel<G_, P_, X_, S_>), grid, block, smem, s, p)
+#define DMM_TQ_XS(G_, P_, S_) \
+    do { if (xlds) DMM_TQ_LAUNCH(G_, P_, true, S_); else DMM_TQ_LAUNCH(G_, P_, false, S_); } while (0)
+    if (a.G == 64) {
+        if (a.planes == 2) { if (sv) DMM_TQ_XS(64, 2, true); else DMM_TQ_XS(64, 2, false); }
+        else { if (sv) DMM_TQ_XS(64, 1, true); else DMM_TQ_XS(64, 1, false); }
+    } else {
+        if (a.planes == 2) DMM_TQ_XS(128, 2, false);
+        else DMM_TQ_XS(128, 1, false);
+    }
+#undef DMM_TQ_XS
+#undef DMM_TQ_LAUNCH
     return hipGetLastError();
 }
 
