@@ -49,8 +49,13 @@ def parse():
     ap.add_argument("--layers", type=int, default=8, help="code matrices per step")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
     ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads)")
+    ap.add_argument("--extras", default="routeb,ternary,moe,prefill",
+                    help="comma list of extra workloads to time (routeb, ternary, moe, prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 512 MiB device-to-device copy five times (a kernel of "
+                         "known traffic, for scaling hardware byte counters) and exit")
     return ap.parse_args()
 
 
@@ -159,6 +164,15 @@ def main():
     torch.cuda.set_device(dev)
     use_graph = not args.no_graph
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "copies": 5}), flush=True)
+        return
+
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
@@ -249,92 +263,97 @@ def _timed_launches(torch, fn, n_launch, use_graph, reps=20, warmup=3):
 
 def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
     res = {}
+    sel = set(args.extras.split(","))
     dev = torch.device("cuda:0")
 
-    progress("extra: routeb_gemv M=4,16")
-    # Route B GEMV at M = 4 (same codes as the headline, 8 layers)
-    d = workloads.routeb_gemv(M=4)
-    table = to_dev(dmm.rb_table(d["ladder"]))
-    c0 = to_dev(d["codes"])
-    bufs = [c0] + [((c0.to(torch.int32) + 37 * i) % 243).to(torch.uint8) for i in range(1, 8)]
-    for M in (4, 16):
-        x = to_dev(bits16(workloads.routeb_gemv(M=M, N=1)["x"]))
-        ys = [torch.empty((M, 8192), dtype=torch.bfloat16, device=dev) for _ in range(8)]
-        fn = lambda: [dmm.rb_matmul(x, bufs[i], table, float(d["alpha"]), ys[i]) for i in range(8)]
-        sec = _timed_launches(torch, fn, 8, use_graph)
-        b = 8192 * 8192 + 972 + M * 8192 * 4
-        res[f"routeb_gemv_M{M}"] = _rec(b, sec, M, 2 * M * 8192 * 8192)
-    del bufs
+    if "routeb" in sel:
+        progress("extra: routeb_gemv M=4,16")
+        # Route B GEMV at M = 4 (same codes as the headline, 8 layers)
+        d = workloads.routeb_gemv(M=4)
+        table = to_dev(dmm.rb_table(d["ladder"]))
+        c0 = to_dev(d["codes"])
+        bufs = [c0] + [((c0.to(torch.int32) + 37 * i) % 243).to(torch.uint8) for i in range(1, 8)]
+        for M in (4, 16):
+            x = to_dev(bits16(workloads.routeb_gemv(M=M, N=1)["x"]))
+            ys = [torch.empty((M, 8192), dtype=torch.bfloat16, device=dev) for _ in range(8)]
+            fn = lambda: [dmm.rb_matmul(x, bufs[i], table, float(d["alpha"]), ys[i]) for i in range(8)]
+            sec = _timed_launches(torch, fn, 8, use_graph)
+            b = 8192 * 8192 + 972 + M * 8192 * 4
+            res[f"routeb_gemv_M{M}"] = _rec(b, sec, M, 2 * M * 8192 * 8192)
+        del bufs
 
-    progress("extra: ternary_gemv")
-    # ternary GEMV 14336 x 4096, codes packed on the GPU, 37 rotating copies
-    d = workloads.ternary_gemv()
-    W = to_dev(d["W"])
-    cs, ss = dmm.packed_shape(14336, 4096, 64)
-    c = torch.empty(cs, dtype=torch.uint8, device=dev)
-    s = torch.empty(ss, dtype=torch.int16, device=dev)
-    st = dmm.tq_pack(W, 64, 1, c, s)
-    assert int(st.item()) == 0
-    del W
-    R = 37
-    cc = [c] + [c.clone() for _ in range(R - 1)]
-    sc = [s] + [s.clone() for _ in range(R - 1)]
-    for M in (1, 4, 16):
-        x = to_dev(bits16(d["x"][:M]))
-        ys = [torch.empty((M, 14336), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fn = lambda: [dmm.tq_matmul(x, cc[i], sc[i], 14336, 64, ys[i]) for i in range(R)]
-        sec = _timed_launches(torch, fn, R, use_graph)
-        b = c.numel() + s.numel() * 2 + M * 4096 * 2 + M * 14336 * 2
-        res[f"ternary_gemv_M{M}"] = _rec(b, sec, M, 2 * M * 14336 * 4096)
-    del cc, sc
+    if "ternary" in sel:
+        progress("extra: ternary_gemv")
+        # ternary GEMV 14336 x 4096, codes packed on the GPU, 37 rotating copies
+        d = workloads.ternary_gemv()
+        W = to_dev(d["W"])
+        cs, ss = dmm.packed_shape(14336, 4096, 64)
+        c = torch.empty(cs, dtype=torch.uint8, device=dev)
+        s = torch.empty(ss, dtype=torch.int16, device=dev)
+        st = dmm.tq_pack(W, 64, 1, c, s)
+        assert int(st.item()) == 0
+        del W
+        R = 37
+        cc = [c] + [c.clone() for _ in range(R - 1)]
+        sc = [s] + [s.clone() for _ in range(R - 1)]
+        for M in (1, 4, 16):
+            x = to_dev(bits16(d["x"][:M]))
+            ys = [torch.empty((M, 14336), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fn = lambda: [dmm.tq_matmul(x, cc[i], sc[i], 14336, 64, ys[i]) for i in range(R)]
+            sec = _timed_launches(torch, fn, R, use_graph)
+            b = c.numel() + s.numel() * 2 + M * 4096 * 2 + M * 14336 * 2
+            res[f"ternary_gemv_M{M}"] = _rec(b, sec, M, 2 * M * 14336 * 4096)
+        del cc, sc
 
-    progress("extra: moe_two_plane (generating 2 GiB of weights)")
-    # two-plane MoE: 64 experts 2048 x 4096, 16 tokens, top-8, 3 rotating copies
-    d = workloads.moe_two_plane()
-    W = to_dev(d["W"].reshape(-1, 4096))
-    cs, ss = dmm.packed_shape(64 * 2048, 4096, 64)
-    pk = []
-    for r in range(3):
-        c1 = torch.empty(cs, dtype=torch.uint8, device=dev)
-        s1 = torch.empty(ss, dtype=torch.int16, device=dev)
-        c2 = torch.empty(cs, dtype=torch.uint8, device=dev)
-        s2 = torch.empty(ss, dtype=torch.int16, device=dev)
-        if r == 0:
-            st = dmm.tq_pack(W, 64, 2, c1, s1, c2, s2)
-            assert int(st.item()) == 0
-        else:
-            c1.copy_(pk[0][0]); s1.copy_(pk[0][1]); c2.copy_(pk[0][2]); s2.copy_(pk[0][3])
-        pk.append((c1, s1, c2, s2))
-    del W
-    x = to_dev(bits16(d["x"]))
-    ids = to_dev(d["ids"])
-    ys = [torch.empty((16, 8, 2048), dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    fn = lambda: [dmm.tq_matmul(x, pk[i][0], pk[i][1], 2048, 64, ys[i], pk[i][2], pk[i][3],
-                                n_experts=64, expert_ids=ids, top_k=8) for i in range(3)]
-    sec = _timed_launches(torch, fn, 3, use_graph)
-    touched = len(set(d["ids"].reshape(-1).tolist()))
-    b = touched * 2 * 2048 * 64 * 15 + 16 * 4096 * 2 + 16 * 8 * 4 + 16 * 8 * 2048 * 2
-    rec = _rec(b, sec, 16, 2 * 16 * 8 * 2048 * 4096)
-    rec["touched_experts"] = touched
-    res["moe_two_plane_T16"] = rec
-    del pk
+    if "moe" in sel:
+        progress("extra: moe_two_plane (generating 2 GiB of weights)")
+        # two-plane MoE: 64 experts 2048 x 4096, 16 tokens, top-8, 3 rotating copies
+        d = workloads.moe_two_plane()
+        W = to_dev(d["W"].reshape(-1, 4096))
+        cs, ss = dmm.packed_shape(64 * 2048, 4096, 64)
+        pk = []
+        for r in range(3):
+            c1 = torch.empty(cs, dtype=torch.uint8, device=dev)
+            s1 = torch.empty(ss, dtype=torch.int16, device=dev)
+            c2 = torch.empty(cs, dtype=torch.uint8, device=dev)
+            s2 = torch.empty(ss, dtype=torch.int16, device=dev)
+            if r == 0:
+                st = dmm.tq_pack(W, 64, 2, c1, s1, c2, s2)
+                assert int(st.item()) == 0
+            else:
+                c1.copy_(pk[0][0]); s1.copy_(pk[0][1]); c2.copy_(pk[0][2]); s2.copy_(pk[0][3])
+            pk.append((c1, s1, c2, s2))
+        del W
+        x = to_dev(bits16(d["x"]))
+        ids = to_dev(d["ids"])
+        ys = [torch.empty((16, 8, 2048), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        fn = lambda: [dmm.tq_matmul(x, pk[i][0], pk[i][1], 2048, 64, ys[i], pk[i][2], pk[i][3],
+                                    n_experts=64, expert_ids=ids, top_k=8) for i in range(3)]
+        sec = _timed_launches(torch, fn, 3, use_graph)
+        touched = len(set(d["ids"].reshape(-1).tolist()))
+        b = touched * 2 * 2048 * 64 * 15 + 16 * 4096 * 2 + 16 * 8 * 4 + 16 * 8 * 2048 * 2
+        rec = _rec(b, sec, 16, 2 * 16 * 8 * 2048 * 4096)
+        rec["touched_experts"] = touched
+        res["moe_two_plane_T16"] = rec
+        del pk
 
-    progress("extra: routeb_prefill")
-    # Route B prefill M = 2048 (MFMA bound)
-    d = workloads.routeb_prefill()
-    table = to_dev(dmm.rb_table(d["ladder"]))
-    cd = to_dev(d["codes"])
-    x = to_dev(bits16(d["x"]))
-    rho = to_dev(bits16(d["row_scale"]))
-    y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=dev)
-    fn = lambda: dmm.rb_matmul(x, cd, table, float(d["alpha"]), y, rho)
-    sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
-    flops = 2.0 * 2048 * 8192 * 8192
-    res["routeb_prefill_M2048"] = {
-        "us_per_launch": round(sec * 1e6, 2),
-        "tflops": round(flops / sec / 1e12, 2),
-        "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-    }
+    if "prefill" in sel:
+        progress("extra: routeb_prefill")
+        # Route B prefill M = 2048 (MFMA bound)
+        d = workloads.routeb_prefill()
+        table = to_dev(dmm.rb_table(d["ladder"]))
+        cd = to_dev(d["codes"])
+        x = to_dev(bits16(d["x"]))
+        rho = to_dev(bits16(d["row_scale"]))
+        y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=dev)
+        fn = lambda: dmm.rb_matmul(x, cd, table, float(d["alpha"]), y, rho)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        flops = 2.0 * 2048 * 8192 * 8192
+        res["routeb_prefill_M2048"] = {
+            "us_per_launch": round(sec * 1e6, 2),
+            "tflops": round(flops / sec / 1e12, 2),
+            "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        }
     return res
 
 

@@ -110,6 +110,8 @@ struct TqMatmulArgs {
 };
 
 hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
+// Streaming dense form for M <= 4; false when the call is outside its domain.
+bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
 int tq_max_grouped_pairs();  // largest M * top_k of a grouped call
 
 struct RbMatmulArgs {

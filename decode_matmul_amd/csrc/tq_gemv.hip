@@ -386,6 +386,10 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
     p.row_blocks = (int)((a.N + 15) / 16);
     p.y = a.y;
     p.y_dtype = a.y_dtype;
+    {
+        hipError_t e;
+        if (launch_tq_rows(a, s, &e)) return e;
+    }
     const int experts = p.grouped ? a.n_experts : 1;
     const int64_t items = (int64_t)p.row_blocks * experts;
     if (items == 0) return hipSuccess;

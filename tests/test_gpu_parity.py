@@ -244,6 +244,23 @@ def test_tq_matmul_small(dmm, M, N, K, G, planes):
         tq_case(dmm, M, N, K, G, planes, ydt, seed=M * 1000 + N + K)
 
 
+# Shapes of the streaming form (dense, M <= 4, K = 1024 .. 4096): every
+# groups-per-row it takes, one and two planes, row counts that leave partial
+# 16-row blocks and partial workgroup ranges, and row ranges of 5 to 8 blocks
+# (more than the four blocks in flight).
+TQ_STREAM_CASES = [
+    (1, 1000, 1024, 1), (2, 777, 2048, 2), (3, 300, 3072, 1), (4, 2050, 4096, 2),
+    (1, 5, 4096, 1), (4, 4100, 4096, 1), (1, 20000, 1024, 1), (2, 33000, 1024, 1),
+    (3, 1, 2048, 2),
+]
+
+
+@pytest.mark.parametrize("M,N,K,planes", TQ_STREAM_CASES)
+def test_tq_matmul_streaming_shapes(dmm, M, N, K, planes):
+    for ydt in (torch.float32, torch.bfloat16):
+        tq_case(dmm, M, N, K, 64, planes, ydt, seed=7 * M + N + K)
+
+
 @pytest.mark.parametrize("code_off,x_off", [(1, 0), (2, 2), (3, 4), (5, 6)])
 def test_tq_matmul_offset_views(dmm, code_off, x_off):
     """Non-zero view offsets of codes (any byte) and x (any 4-byte step)."""
