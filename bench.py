@@ -36,6 +36,12 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes of one headline launch (M = 1) from the hardware byte counters
+# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the factors that make a 512 MiB device
+# copy read and write 512 MiB), in profiles/hbm_traffic_rb_gemv_tq_rows.md.
+# The figure belongs to the kernel source it was measured on: any other
+# source of rb_gemv.hip reports null.
+MEASURED_TRAFFIC = {"rb_gemv.hip": ("6aba783a075bef5a", 67368885)}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "packed matmul: weight GB/s vs HBM peak at M=1–16; TFLOP/s at M=2048"
 
@@ -61,6 +67,21 @@ def parse():
 
 def bits16(a):
     return np.ascontiguousarray(a).view(np.int16)
+
+
+def measured_traffic(src, M):
+    """Counter-derived HBM bytes per launch, or None when the kernel source
+    differs from the measured one or the launch is not the measured M = 1."""
+    import hashlib
+    if M != 1 or src not in MEASURED_TRAFFIC:
+        return None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_matmul_amd", "csrc", src)
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    want, nbytes = MEASURED_TRAFFIC[src]
+    return nbytes if digest == want else None
 
 
 def progress(msg):
@@ -231,8 +252,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "rb_gemv_kernel",
+            "traffic": measured_traffic("rb_gemv.hip", M),
+            "kernel": "rb_gemv_tiled_kernel",
             "bytes_per_launch": bytes_launch,
             "us_per_launch": round(per_launch * 1e6, 3),
             "tok_s_equiv_per_layer": round(M / per_launch, 1),

@@ -146,6 +146,7 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) A[q] = *(const u32x4*)(xp + 8 * q);
     }
+    __builtin_amdgcn_sched_barrier(0);     // activations are issued before the code stream
 
     // ---- this thread's chunks of every block, and the first kNSB blocks
     Chunk ch[SPB];
