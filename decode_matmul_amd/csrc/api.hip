@@ -153,7 +153,7 @@ int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int
         if ((N + 15) / 16 >= kMaxDim) return TQ_ERR_SHAPE;
         return hip_status(dmm::launch_rb_gemv(a, s));
     }
-    if ((M + 127) / 128 >= 65536) return TQ_ERR_SHAPE;
+    if ((M + 255) / 256 >= 65536) return TQ_ERR_SHAPE;
     return hip_status(dmm::launch_rb_prefill(a, s));
 }
 

@@ -1,32 +1,63 @@
 // Route B prefill (M > 16): y[m, n] = alpha * rho_n * sum_k x[m, k] T[codes[n, k]] + bias_n
-// as a bf16 MFMA GEMM whose weight tiles are decoded from code bytes into LDS.
+// as an MFMA GEMM whose weight tiles are decoded from code bytes into LDS.
 //
 // Semantics: "A Discrete Weight Language for Large Language Models" (Route
 // B), section 4.2: the code book is loaded on chip once per block and a
 // K-sliced GEMM dereferences every code byte through it; rho_n is applied to
 // the output accumulator before the bias add (section 3.3).
 //
+// Numerics.  The products run on fp16 MFMAs with fp32 accumulation:
+//  * The code book is scaled by sigma = 2^j so that max |sigma T| lies in
+//    [2^14, 2^15) and each entry is rounded to fp16 once (relative error at
+//    most 2^-11, against the 2e-3 acceptance bound).  The output is scaled
+//    back by 1/sigma exactly.
+//  * bf16 activations are converted to fp16 exactly when 2^-17 <= |x| <=
+//    65280 or x = 0 (fp16 holds every such bf16 value).
+//  * An 8-value activation chunk outside that range (every chunk, when a
+//    nonzero code-book entry falls below the fp16 normal range after
+//    scaling) enters the fp16 pass as zeros and is added afterwards on bf16
+//    MFMAs in two passes: the bf16 activations against hi = bf16(sigma T),
+//    then against lo = bf16(sigma T - hi) (together within 2^-17 of
+//    sigma T), with every other chunk zero.  So every input meets the bound;
+//    typical activations take only the fp16 pass.
+//
 // Mapping onto gfx950:
-//  * 256-thread workgroups own a 128 x 128 tile of y (tokens x rows); 4 waves
-//    in a 2 x 2 grid each own 64 x 64 = 4 x 4 MFMA 16x16x32 tiles.
-//  * Per K-slice of 64: the activation tile is copied to LDS; the code tile
-//    (128 rows x 64 bytes) is decoded through a 32-copy bank-replicated LDS
-//    table of bf16 code-book values into a bf16 weight tile in LDS.  The
-//    next slice's global loads are issued before the current MFMAs.
-//  * Weight values are bf16 of the fp32 table entry (relative error up to
-//    2^-8 per term, for entries just above a power of two); accumulation is
-//    fp32.  Uniform codes and Gaussian activations average these errors far
-//    below the 2e-3 sum|x w| bound, but a constant-code input can exceed it.
+//  * A 512-thread workgroup (8 waves in a 2 x 4 grid, two per SIMD so one
+//    wave's decode overlaps the other's MFMAs) owns a 256 x 256 tile of y
+//    (tokens x rows); each wave owns 128 x 64 = 4 x 2 MFMA 32x32x16 tiles
+//    (128 fp32 accumulators per lane).
+//  * K-slices of 32: the activation tile (256 x 32, converted to fp16) and
+//    the weight tile (256 rows x 32 codes, decoded through the LDS code
+//    book) are written to one of two LDS buffers while the MFMAs read the
+//    other; the next slice's global loads are issued before the MFMAs.  One
+//    barrier per slice.
+//  * The code book sits in LDS in 32 copies: entry b of copy c at byte
+//    (b << 8) | (c << 2) holds the fp16 value, and 128 bytes further the
+//    (hi, lo) bf16 pair.  One v_perm of the code word and the lane offset
+//    forms the address; the 32 lanes of a phase hit distinct banks.
+//  * Tile rows are 80 bytes apart, so the 8 lanes of a 16-byte column read
+//    cover all 32 banks.
 #include "common.h"
 
 namespace dmm {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDT = BK + 8;                  // LDS row pitch in bf16 (144 B)
-constexpr int kThreads = 256;
-constexpr int kCopies = 32;
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int kThreads = 512;
+constexpr int kWN = 4;                         // waves along N (2 along M)
+constexpr int MT = 4, NT = 2;                  // 32x32 MFMA tiles per wave along M and N
+constexpr int kPitch = 2 * BK + 16;            // bytes per LDS tile row
+constexpr int kTileBytes = BM * kPitch;        // one operand tile (BM == BN)
+constexpr int kLutBytes = 256 * 256;
+constexpr int kMapSlices = 1536;                // slices tracked one by one (K <= 49152)
+constexpr int kSmemBytes = kLutBytes + 4 * kTileBytes + 96 + 8 * (kMapSlices + 1);
+static_assert(kThreads / 64 <= 8, "one flag byte per wave");
+static_assert(kMapSlices * 2 <= 2 * kTileBytes, "the slice list fits LDS buffer 1");
+static_assert(BM == BN, "square tiles share one pitch");
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct Params {
     const uint16_t* x;
@@ -38,145 +69,352 @@ struct Params {
     const float* bias;
     void* y;
     int y_dtype;
-    int aligned;                             // x, codes 16-B aligned and K % 16 == 0
 };
 
-__global__ void __launch_bounds__(kThreads, 2)
-rb_prefill_kernel(Params p) {
-    __shared__ uint32_t lut[256 * kCopies];                     // 32 KB
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDT];
+// Per-thread loads of one K-slice: 2 chunks of 8 activations, 1 chunk of 16 codes.
+constexpr int XCH = BM * BK / 8 / kThreads, CCH = BN * BK / 16 / kThreads;
+struct Slice {
+    u32x4 xa[XCH];
+    u32x4 cd[CCH];
+};
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running range of the activations of one chunk (bf16 bits with the sign
+// cleared, two halves per word): the largest value, and the smallest
+// nonzero value minus one (a zero wraps to 0xffff and drops out).
+struct Range {
+    u16x2 hi = {0, 0};
+    u16x2 lo = {0xffff, 0xffff};
+};
+
+// Two bf16 activations -> two fp16 (exact inside the range that R checks).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d, Range& R) {
+    const u16x2 t = __builtin_bit_cast(u16x2, d & 0x7fff7fffu);
+    R.hi = __builtin_elementwise_max(R.hi, t);
+    R.lo = __builtin_elementwise_min(R.lo, (u16x2)(t - (u16x2){1, 1}));
+    const float a = __builtin_bit_cast(float, d << 16);
+    const float b = __builtin_bit_cast(float, d & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// True when every activation seen is 0 or has 2^-17 <= |x| <= 65280
+// (bf16 bits 0x3700 .. 0x477f), i.e. is exact in fp16.
+__device__ __forceinline__ bool range_ok(const Range& R) {
+    return max(R.hi.x, R.hi.y) <= 0x477f && min(R.lo.x, R.lo.y) >= 0x36ff;
+}
+
+template <bool AL>
+__global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
+    // one LDS block: the code book at address 0 (so a v_perm result is its
+    // own address), two buffers of (activation, weight) tiles, a few words
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+    unsigned char* const lut = smem;
+    typedef unsigned char Tile[kTileBytes];
+    Tile* const tiles2 = (Tile*)(smem + kLutBytes);            // [buf * 2 + (0: A, 1: B)]
+    unsigned char* const words = smem + kLutBytes + 4 * kTileBytes;
+    int& table_bad = *(int*)(words);
+    int& redo_n = *(int*)(words + 8);
+    float* const red_max = (float*)(words + 64);
+    // one flag word per slice s < kMapSlices, one byte per wave (written by
+    // the whole wave, so no atomics); word kMapSlices collects later slices
+    uint64_t* const bad_map = (uint64_t*)(words + 96);
+    uint16_t* const redo = (uint16_t*)tiles2[2];        // list of flagged slices (buffer 1, idle then)
 
     const int tid = threadIdx.x;
-    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
 
-    for (int i = tid; i < 256 * kCopies; i += kThreads) {
-        const int b = i / kCopies;
-        lut[i] = b < 243 ? (uint32_t)f32_to_bf16_rne(p.table[b]) : 0u;
+    // ---- code book scale: sigma = 2^j with max |sigma T| in [2^14, 2^15)
+    float tv = 0.f;
+    if ((tid & 255) < 243) tv = p.table[tid & 255];
+    {
+        float a = fabsf(tv);
+        for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+        if (lane == 0) red_max[wave] = a;
+        if (tid == 0) { table_bad = 0; redo_n = 0; }
+        for (int i = tid; i <= kMapSlices; i += kThreads) bad_map[i] = 0ull;
+    }
+    __syncthreads();
+    float tmax = red_max[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) tmax = fmaxf(tmax, red_max[w]);
+    int e2 = 0;
+    if (tmax > 0.f && tmax <= 3.0e38f) (void)frexpf(tmax, &e2);     // tmax < 2^e2
+    const int j = min(max(15 - e2, -120), 120);
+    const float sigma = ldexpf(1.f, j), inv_sigma = ldexpf(1.f, -j);
+    {
+        // entry tid (zero for the 13 padding codes): fp16 of sigma T and the bf16 hi/lo pair
+        const float s = tv * sigma;                                   // exact power-of-two scaling
+        const _Float16 h = (_Float16)s;                               // nearest-even
+        const uint32_t hb = __builtin_bit_cast(uint16_t, h);
+        const bool ok = (s == 0.f) || (fabsf(s) >= 0x1p-14f && fabsf(s) <= 65504.f);
+        if ((tid & 255) < 243 && !ok) table_bad = 1;
+        const uint16_t hi = f32_to_bf16_rne(s);
+        const uint16_t lo = f32_to_bf16_rne(s - bf16_bits_to_f32(hi));
+        const uint32_t fb = (uint32_t)hi | ((uint32_t)lo << 16);
+        // entry tid & 255, copies 16 (tid >> 8) .. +15
+        const int b = tid & 255;
+#pragma unroll 4
+        for (int c = 16 * (tid >> 8); c < 16 * (tid >> 8) + 16; ++c) {
+            *(uint32_t*)(lut + ((b << 8) | (c << 2))) = hb;
+            *(uint32_t*)(lut + ((b << 8) | 128 | (c << 2))) = fb;
+        }
     }
 
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int lr = tid >> 1;                 // tile row this thread loads
-    const int lh = tid & 1;                  // which 32-column half
-    const bool m_full = m0 + BM <= p.M;
-    const bool n_full = n0 + BN <= p.N;
-    // lane constant for the LUT address: copy (lane & 31), entry stride 128 B
-    const uint32_t lane_c = (uint32_t)(lane & 31) << 3;
+    const int nslices = (int)((p.K + BK - 1) / BK);
+    const uint32_t cofs = (uint32_t)(lane & 31) << 2;
 
-    u32x4 ra[4], rc[2];
-    auto gload = [&](int64_t k0) {
-        const bool full = p.aligned && m_full && n_full && (k0 + BK <= p.K);
-        const int64_t m = m0 + lr, n = n0 + lr;
-        const int64_t k = k0 + 32 * lh;
-        if (full) {
-            const u32x4* xp = (const u32x4*)(p.x + m * p.K + k);
+    // this thread's chunks: activations (rows xr + 128 i, 8 values at column
+    // 8 xc), codes (row cr, 16 bytes at column 16 cc)
+    const int xc = tid & 3, xr = tid >> 2;
+    const int cc = tid & 1, cr = tid >> 1;
+    static_assert(XCH == 2 && CCH == 1, "chunk mapping");
+
+    auto gload = [&](int s, Slice& S) {
+        const int64_t k0 = (int64_t)min(s, nslices - 1) * BK;
+        if constexpr (AL) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ra[i] = xp[i];
-            const u32x4* cp = (const u32x4*)(p.codes + n * p.K + k);
-            rc[0] = cp[0];
-            rc[1] = cp[1];
+            for (int i = 0; i < XCH; ++i) {
+                const int64_t m = min(m0 + xr + 128 * i, p.M - 1);
+                S.xa[i] = *(const u32x4*)(p.x + m * p.K + k0 + 8 * xc);
+            }
+#pragma unroll
+            for (int i = 0; i < CCH; ++i) {
+                const int64_t n = min(n0 + cr + 256 * i, p.N - 1);
+                S.cd[i] = *(const u32x4*)(p.codes + n * p.K + k0 + 16 * cc);
+            }
         } else {
+            // element loads: activations past M or K are 0, codes past N or K
+            // are 255 (a zero entry of the padded table)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < XCH; ++i) {
+                const int64_t m = m0 + xr + 128 * i;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t kk = k + 8 * i + 2 * j;
+                for (int w = 0; w < 4; ++w) {
+                    const int64_t k = k0 + 8 * xc + 2 * w;
                     uint32_t lo = 0, hi = 0;
                     if (m < p.M) {
-                        if (kk < p.K) lo = p.x[m * p.K + kk];
-                        if (kk + 1 < p.K) hi = p.x[m * p.K + kk + 1];
+                        if (k < p.K) lo = p.x[m * p.K + k];
+                        if (k + 1 < p.K) hi = p.x[m * p.K + k + 1];
                     }
-                    ra[i][j] = lo | (hi << 16);
+                    S.xa[i][w] = lo | (hi << 16);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < CCH; ++i) {
+                const int64_t n = n0 + cr + 256 * i;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t w = 0;
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t v = 0;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const int64_t kk = k + 16 * i + 4 * j + b;
-                        const uint32_t c = (n < p.N && kk < p.K) ? p.codes[n * p.K + kk] : 0xffu;
-                        w |= c << (8 * b);
+                        const int64_t k = k0 + 16 * cc + 4 * w + b;
+                        const uint32_t c = (n < p.N && k < p.K) ? p.codes[n * p.K + k] : 0xffu;
+                        v |= c << (8 * b);
                     }
-                    rc[i][j] = w;
+                    S.cd[i][w] = v;
                 }
             }
         }
     };
 
-    f32x4 acc[4][4];
+    // weight tile of a slice from the code book: fp16 (word 0) or bf16 hi / lo
+    // (word at + 128, part 0 / 1)
+    auto store_weights = [&](int buf, const Slice& S, uint32_t lut_off, uint32_t sel) {
+        unsigned char* B = tiles2[2 * buf + 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < CCH; ++i) {
+            u32x4 o0, o1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t d = S.cd[i][w];
+                uint32_t e[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    e[b] = *(const uint32_t*)(lut + lut_off +
+                                              perm_b32(d, cofs, 0x0c0c0400u + ((uint32_t)b << 8)));
+                const uint32_t p01 = perm_b32(e[1], e[0], sel);
+                const uint32_t p23 = perm_b32(e[3], e[2], sel);
+                if (w < 2) { o0[2 * w] = p01; o0[2 * w + 1] = p23; }
+                else { o1[2 * w - 4] = p01; o1[2 * w - 3] = p23; }
+            }
+            unsigned char* dst = B + (cr + 256 * i) * kPitch + 32 * cc;
+            *(u32x4*)dst = o0;
+            *(u32x4*)(dst + 16) = o1;
+        }
+    };
 
-    const unsigned char* lutb = (const unsigned char*)lut;
-    gload(0);
-    for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
-        __syncthreads();                              // previous slice consumed
-        {
-            u32x4* ad = (u32x4*)(As + lr * LDT + 32 * lh);
+    // fp16 activations and weights of a slice into buffer buf.  A chunk of 8
+    // activations outside the exact range (or every chunk, when the code book
+    // does not fit fp16) is written as zeros and counted for the bf16 pass.
+    auto store_f16 = [&](int s, int buf, const Slice& S, bool force_bad) {
+        unsigned char* A = tiles2[2 * buf];
+        int nbad = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ad[i] = ra[i];
-            u32x4* bd = (u32x4*)(Bs + lr * LDT + 32 * lh);
+        for (int i = 0; i < XCH; ++i) {
+            Range R;
+            u32x4 v;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int w = 0; w < 4; ++w) v[w] = bf16x2_to_f16x2(S.xa[i][w], R);
+            const bool bad = force_bad | !range_ok(R);     // no short circuit: no branch
+            nbad += bad;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t w = rc[i][j];
-                    uint32_t e[4];
+            for (int w = 0; w < 4; ++w) v[w] = bad ? 0u : v[w];
+            *(u32x4*)(A + (xr + 128 * i) * kPitch + 16 * xc) = v;
+        }
+        // the wave's flag for this slice, stored by every lane (same value);
+        // the word past the map keeps an OR of every later slice
+        const bool wbad = __builtin_amdgcn_ballot_w64(nbad != 0) != 0;
+        unsigned char* fb = (unsigned char*)&bad_map[min(s, kMapSlices)] + wave;
+        *fb = (unsigned char)((s >= kMapSlices ? *fb : 0) | (wbad ? 1 : 0));
+        store_weights(buf, S, 0u, 0x05040100u);
+    };
+
+    // the bf16 pass: bf16 activations of the chunks the fp16 pass left out
+    // (zeros elsewhere) and the hi (part 0) or lo (part 1) bf16 weights
+    auto store_bf16 = [&](int buf, const Slice& S, bool force_bad, int part) {
+        unsigned char* A = tiles2[2 * buf];
+        if (part == 0) {
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const uint32_t a2 = perm_b32(w, lane_c, 0x0c0c0400u + ((uint32_t)b << 8));
-                        e[b] = *(const uint32_t*)(lutb + (a2 >> 1));
-                    }
-                    const uint32_t p01 = perm_b32(e[1], e[0], 0x05040100u);
-                    const uint32_t p23 = perm_b32(e[3], e[2], 0x05040100u);
-                    ((uint32_t*)bd)[8 * i + 2 * j] = p01;
-                    ((uint32_t*)bd)[8 * i + 2 * j + 1] = p23;
-                }
+            for (int i = 0; i < XCH; ++i) {
+                Range R;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) (void)bf16x2_to_f16x2(S.xa[i][w], R);
+                const bool bad = force_bad | !range_ok(R);     // no short circuit: no branch
+                u32x4 v;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[w] = bad ? S.xa[i][w] : 0u;
+                *(u32x4*)(A + (xr + 128 * i) * kPitch + 16 * xc) = v;
             }
         }
-        __syncthreads();
-        if (k0 + BK < p.K) gload(k0 + BK);
+        store_weights(buf, S, 128u, part == 0 ? 0x05040100u : 0x07060302u);
+    };
+
+    // accumulators start life in the accumulation registers (the empty asm
+    // pins the register class), so the loop never copies them through VGPRs
+    f32x16 acc[MT][NT];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int kc = kk * 32 + (lane >> 4) * 8;
-            u32x4 af[4], bfv[4];
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                af[mb] = *(const u32x4*)(As + (wm * 64 + mb * 16 + (lane & 15)) * LDT + kc);
+        for (int jn = 0; jn < NT; ++jn) {
+            f32x16 z;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-                bfv[nb] = *(const u32x4*)(Bs + (wn * 64 + nb * 16 + (lane & 15)) * LDT + kc);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, af[mb]), __builtin_bit_cast(bf16x8, bfv[nb]),
-                        acc[mb][nb], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            asm volatile("" : "+a"(z));
+            acc[i][jn] = z;
         }
+
+    // A fragment: lane l holds A[l % 32][8 (l / 32) .. +7]; B alike with the
+    // rows of the weight tile
+    const int frow = lane & 31;
+    const int fk = 16 * (lane >> 5);
+    auto mfma_slice = [&](int buf, bool f16) {
+        const unsigned char* A = tiles2[2 * buf] + (wm * 32 * MT + frow) * kPitch + fk;
+        const unsigned char* B = tiles2[2 * buf + 1] + (wn * 32 * NT + frow) * kPitch + fk;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            u32x4 af[MT], bf[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) af[i] = *(const u32x4*)(A + i * 32 * kPitch + 32 * ks);
+#pragma unroll
+            for (int jn = 0; jn < NT; ++jn) bf[jn] = *(const u32x4*)(B + jn * 32 * kPitch + 32 * ks);
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int jn = 0; jn < NT; ++jn) {
+                    if (f16)
+                        acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8, af[i]), __builtin_bit_cast(f16x8, bf[jn]),
+                            acc[i][jn], 0, 0, 0);
+                    else
+                        acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bf[jn]),
+                            acc[i][jn], 0, 0, 0);
+                }
+        }
+    };
+
+    __syncthreads();                       // table and flags written
+    const bool all_bf16 = readfirstlane(table_bad) != 0;   // uniform: LDS values are not known to be
+
+    // ---- fp16 pass over every slice (out-of-range chunks enter as zeros)
+    Slice S;
+    if (nslices > 0) {                     // K = 0 reads nothing (x may be null)
+        gload(0, S);
+        store_f16(0, 0, S, all_bf16);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s < nslices; ++s) {
+        const int buf = s & 1;
+        gload(s + 1, S);                   // next slice (clamped; unused past the end)
+        mfma_slice(buf, true);
+        // past the last slice this rewrites the last slice's data into the
+        // idle buffer and flags it again: harmless, and keeps the body free
+        // of branches so the decode interleaves with the MFMAs
+        store_f16(min(s + 1, nslices - 1), buf ^ 1, S, all_bf16);
+        // interleave: fragment reads first, then per MFMA about six VALU
+        // operations and one table read, the tile writes last
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MT + NT), 0);
+#pragma unroll
+        for (int g = 0; g < 2 * MT * NT; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __syncthreads();
     }
 
+    // ---- bf16 pass over the chunks left out: the flagged slices below
+    // kMapSlices one by one, every slice from kMapSlices on if any there was
+    // flagged (a slice without flagged chunks adds zero, so extra ones are
+    // harmless)
+    if (tid == 0) {
+        int n = 0;
+        const int mapped = min(nslices, kMapSlices);
+        for (int w = 0; w < mapped; ++w)
+            if (bad_map[w]) redo[n++] = (uint16_t)w;
+        redo_n = n;
+    }
+    __syncthreads();
+    auto redo_slice = [&](int s) {
+        gload(s, S);
+        store_bf16(0, S, all_bf16, 0);
+        __syncthreads();
+        mfma_slice(0, false);
+        __syncthreads();
+        store_bf16(0, S, all_bf16, 1);
+        __syncthreads();
+        mfma_slice(0, false);
+        __syncthreads();
+    };
+    const int nlist = readfirstlane(redo_n);
+#pragma unroll 1
+    for (int r = 0; r < nlist; ++r) redo_slice(readfirstlane(redo[r]));
+    const int late_end = readfirstlane(bad_map[kMapSlices] != 0ull ? 1 : 0) ? nslices : kMapSlices;
+#pragma unroll 1
+    for (int s = kMapSlices; s < late_end; ++s) redo_slice(s);
+
+    // ---- epilogue: C[m][n] of tile (i, jn) in register r of lane l is
+    // m = 8 (r / 4) + 4 (l / 32) + r % 4, n = l % 32
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
+    for (int jn = 0; jn < NT; ++jn) {
+        const int64_t n = n0 + wn * 32 * NT + jn * 32 + (lane & 31);
         if (n >= p.N) continue;
         const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
         const float bias = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int i = 0; i < MT; ++i) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t m = m0 + wm * 64 + mb * 16 + 4 * (lane >> 4) + i;
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * 32 * MT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (m >= p.M) continue;
-                float v = acc[mb][nb][i] * rho;
+                float v = acc[i][jn][r] * inv_sigma;      // exact
+                v = v * rho;
                 v = v * p.alpha;
                 v = v + bias;
                 const int64_t idx = m * p.N + n;
@@ -202,12 +440,16 @@ hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s) {
     p.bias = a.bias;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
-    p.aligned = (((uintptr_t)a.x & 15) == 0) && (((uintptr_t)a.codes & 15) == 0) &&
-                (a.K % 16 == 0);
+    const bool aligned = (((uintptr_t)a.x & 15) == 0) && (((uintptr_t)a.codes & 15) == 0) &&
+                         (a.K % BK == 0);
     const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
     if (gx == 0 || gy == 0) return hipSuccess;
-    hipLaunchKernelGGL(rb_prefill_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s,
-                       p);
+    if (aligned)
+        hipLaunchKernelGGL(rb_prefill_kernel<true>, dim3((unsigned)gx, (unsigned)gy),
+                           dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(rb_prefill_kernel<false>, dim3((unsigned)gx, (unsigned)gy),
+                           dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -422,6 +422,68 @@ def test_rb_matmul_offsets_and_bad_codes(dmm, code_off, x_off):
     rb_case(dmm, 40, 50, 256, 32, code_off=code_off, x_off=x_off, rho=True)
 
 
+def rb_custom(dmm, xb, codes, table, alpha, what, ydt=torch.float32):
+    """rb_matmul on given bf16 bits, codes and a 243-entry table, against the oracle."""
+    M, K = xb.shape
+    N = codes.shape[0]
+    y = torch.empty((M, N), dtype=ydt, device=DEV)
+    say(f"rb_matmul {what} M={M} N={N} K={K} y={ydt}")
+    dmm.rb_matmul(dev(bits16(xb)), dev(codes), dev(np.asarray(table, np.float32)),
+                  np.float32(alpha), y)
+    y_ref, B = oracle.matmul_ref(xb, oracle.rb_weights(codes, table, alpha))
+    return assert_bound(y_host(y), y_ref, B, what, stored_of(y))
+
+
+BOUND_SHAPES = [(4, 64, 512), (40, 64, 512), (300, 130, 320)]   # GEMV and prefill
+
+
+@pytest.mark.parametrize("M,N,K", BOUND_SHAPES)
+def test_rb_matmul_constant_worst_code(dmm, M, N, K):
+    """Every weight is the code-book entry whose bf16 rounding is worst
+    (relative error 0.0036 > 2e-3 for this ladder) and every activation is
+    positive, so no error cancels: the bound must hold by construction."""
+    table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
+    tb = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(table.astype(np.float64)))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(table != 0, np.abs(tb - table) / np.abs(table), 0.0)
+    worst = int(np.argmax(rel))
+    assert rel[worst] > 2e-3
+    rng = np.random.default_rng(M + N + K)
+    xb = workloads.bf16_bits(np.abs(rng.standard_normal((M, K))).astype(np.float32))
+    codes = np.full((N, K), worst, np.uint8)
+    r = rb_custom(dmm, xb, codes, table, 0.02, f"constant code {worst}")
+    assert r["max_err_over_B"] < 1e-3
+
+
+@pytest.mark.parametrize("M,N,K", BOUND_SHAPES)
+def test_rb_matmul_activations_outside_fp16(dmm, M, N, K):
+    """Activations fp16 cannot hold exactly (above 65280, below 2^-17, far
+    below, exact zeros) scattered through x, and one row entirely huge."""
+    rng = np.random.default_rng(3 * M + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    specials = np.array([1e5, -7e4, 3e-6, -1e-30, 0.0, 65536.0, 2.0 ** -17, 1e30],
+                        np.float32)
+    idx = rng.integers(0, M * K, 40)
+    x.reshape(-1)[idx] = specials[rng.integers(0, len(specials), 40)]
+    x[M // 2] *= np.float32(1e6)
+    xb = workloads.bf16_bits(x)
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
+    rb_custom(dmm, xb, codes, table, 0.02, "activations outside fp16")
+    rb_custom(dmm, xb, codes, table, 0.02, "activations outside fp16", torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", BOUND_SHAPES)
+def test_rb_matmul_wide_code_book(dmm, M, N, K):
+    """A code book spanning more than fp16's range (1e30 next to 1e-30)."""
+    rng = np.random.default_rng(5 * M + N)
+    table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32)).copy()
+    table[0], table[1], table[2] = 1e30, -1e-30, 3e-9
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    rb_custom(dmm, xb, codes, table, 0.5, "wide code book")
+
+
 def test_rb_matmul_routeb_gemv_full(dmm):
     """routeb_gemv: N = K = 8192 at M = 1 and 4, fp32 and bf16 outputs."""
     d = workloads.routeb_gemv()
@@ -472,6 +534,12 @@ def test_zero_sizes_and_empty_k(dmm):
     tbl = torch.zeros(243, dtype=torch.float32, device=DEV)
     dmm.rb_matmul(x0, torch.zeros((3, 0), dtype=torch.uint8, device=DEV), tbl, 0.5, y, None, bias)
     assert np.array_equal(host(y), np.array([[1.0, -2.0, 3.0]] * 2, np.float32))
+    # K = 0 at a prefill size (M > 16)
+    say("prefill K = 0")
+    y40 = torch.full((40, 3), 7.0, dtype=torch.float32, device=DEV)
+    dmm.rb_matmul(torch.zeros((40, 0), dtype=torch.bfloat16, device=DEV),
+                  torch.zeros((3, 0), dtype=torch.uint8, device=DEV), tbl, 0.5, y40, None, bias)
+    assert np.array_equal(host(y40), np.array([[1.0, -2.0, 3.0]] * 40, np.float32))
 
 
 def test_bit_determinism(dmm):
