@@ -26,11 +26,12 @@
 //    wave's decode overlaps the other's MFMAs) owns a 256 x 256 tile of y
 //    (tokens x rows); each wave owns 128 x 64 = 4 x 2 MFMA 32x32x16 tiles
 //    (128 fp32 accumulators per lane).
-//  * K-slices of 32: the activation tile (256 x 32, converted to fp16) and
-//    the weight tile (256 rows x 32 codes, decoded through the LDS code
-//    book) are written to one of two LDS buffers while the MFMAs read the
-//    other; the next slice's global loads are issued before the MFMAs.  One
-//    barrier per slice.
+//  * K-slices of 32 in two LDS buffers: slice t's activation tile (256 x 32,
+//    converted to fp16) and weight tile (256 rows x 32 codes, decoded
+//    through the LDS code book) sit in buffer t & 1.  While the MFMAs of
+//    slice s run from registers, the next K-step's fragments are read and
+//    slice s + 2 (loaded from global memory an iteration earlier) is decoded
+//    into the buffer slice s has just vacated.  One barrier per slice.
 //  * The code book sits in LDS in 32 copies: entry b of copy c at byte
 //    (b << 8) | (c << 2) holds the fp16 value, and 128 bytes further the
 //    (hi, lo) bf16 pair.  One v_perm of the code word and the lane offset
@@ -309,70 +310,78 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
         }
 
     // A fragment: lane l holds A[l % 32][8 (l / 32) .. +7]; B alike with the
-    // rows of the weight tile
+    // rows of the weight tile.  One K-step (16) of a slice per Frag.
     const int frow = lane & 31;
     const int fk = 16 * (lane >> 5);
-    auto mfma_slice = [&](int buf, bool f16) {
-        const unsigned char* A = tiles2[2 * buf] + (wm * 32 * MT + frow) * kPitch + fk;
-        const unsigned char* B = tiles2[2 * buf + 1] + (wn * 32 * NT + frow) * kPitch + fk;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            u32x4 af[MT], bf[NT];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) af[i] = *(const u32x4*)(A + i * 32 * kPitch + 32 * ks);
-#pragma unroll
-            for (int jn = 0; jn < NT; ++jn) bf[jn] = *(const u32x4*)(B + jn * 32 * kPitch + 32 * ks);
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int jn = 0; jn < NT; ++jn) {
-                    if (f16)
-                        acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, af[i]), __builtin_bit_cast(f16x8, bf[jn]),
-                            acc[i][jn], 0, 0, 0);
-                    else
-                        acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bf[jn]),
-                            acc[i][jn], 0, 0, 0);
-                }
-        }
+    struct Frag {
+        u32x4 a[MT];
+        u32x4 b[NT];
     };
+    auto load_frag = [&](int abuf, int bbuf, int ks, Frag& F) {
+        const unsigned char* A = tiles2[2 * abuf] + (wm * 32 * MT + frow) * kPitch + fk + 32 * ks;
+        const unsigned char* B = tiles2[2 * bbuf + 1] + (wn * 32 * NT + frow) * kPitch + fk + 32 * ks;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) F.a[i] = *(const u32x4*)(A + i * 32 * kPitch);
+#pragma unroll
+        for (int jn = 0; jn < NT; ++jn) F.b[jn] = *(const u32x4*)(B + jn * 32 * kPitch);
+    };
+    auto mfma_frag = [&](const Frag& F, bool f16) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int jn = 0; jn < NT; ++jn) {
+                if (f16)
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, F.a[i]), __builtin_bit_cast(f16x8, F.b[jn]),
+                        acc[i][jn], 0, 0, 0);
+                else
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, F.a[i]), __builtin_bit_cast(bf16x8, F.b[jn]),
+                        acc[i][jn], 0, 0, 0);
+            }
+    };
+    static_assert(BK == 32, "two K-steps of 16 per slice");
 
     __syncthreads();                       // table and flags written
     const bool all_bf16 = readfirstlane(table_bad) != 0;   // uniform: LDS values are not known to be
 
-    // ---- fp16 pass over every slice (out-of-range chunks enter as zeros)
+    // ---- fp16 pass over every slice (out-of-range chunks enter as zeros).
+    // Slice t sits in buffer t & 1.  Iteration s runs the MFMAs of slice s
+    // from registers while reading the next fragments; between its two
+    // K-steps one barrier marks buffer s & 1 as read by every wave, and
+    // slice s + 2 is decoded into it.
     Slice S;
+    Frag F0, F1;
     if (nslices > 0) {                     // K = 0 reads nothing (x may be null)
         gload(0, S);
         store_f16(0, 0, S, all_bf16);
+        gload(1, S);
+        store_f16(min(1, nslices - 1), 1, S, all_bf16);
+        gload(2, S);
     }
     __syncthreads();
+    load_frag(0, 0, 0, F0);
 #pragma unroll 1
     for (int s = 0; s < nslices; ++s) {
         const int buf = s & 1;
-        gload(s + 1, S);                   // next slice (clamped; unused past the end)
-        mfma_slice(buf, true);
-        // past the last slice this rewrites the last slice's data into the
-        // idle buffer and flags it again: harmless, and keeps the body free
-        // of branches so the decode interleaves with the MFMAs
-        store_f16(min(s + 1, nslices - 1), buf ^ 1, S, all_bf16);
-        // interleave: fragment reads first, then per MFMA about six VALU
-        // operations and one table read, the tile writes last
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MT + NT), 0);
-#pragma unroll
-        for (int g = 0; g < 2 * MT * NT; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __syncthreads();
+        load_frag(buf, buf, 1, F1);        // slice s, second K-step
+        mfma_frag(F0, true);
+        __syncthreads();                   // every wave is done reading buffer buf
+        // decode slice s + 2 into buffer buf (past the end: the last slice
+        // again, into a buffer nobody reads; no branch, so the decode
+        // interleaves with the MFMAs)
+        store_f16(min(s + 2, nslices - 1), buf, S, all_bf16);
+        load_frag(buf ^ 1, buf ^ 1, 0, F0); // slice s + 1, first K-step
+        mfma_frag(F1, true);
+        gload(s + 3, S);                   // clamped; unused past the end
     }
 
     // ---- bf16 pass over the chunks left out: the flagged slices below
     // kMapSlices one by one, every slice from kMapSlices on if any there was
     // flagged (a slice without flagged chunks adds zero, so extra ones are
-    // harmless)
+    // harmless).  The activations and hi weights go to buffer 0, the lo
+    // weights to the weight tile of buffer 1.
+    __syncthreads();
     if (tid == 0) {
         int n = 0;
         const int mapped = min(nslices, kMapSlices);
@@ -381,23 +390,31 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
         redo_n = n;
     }
     __syncthreads();
-    auto redo_slice = [&](int s) {
-        gload(s, S);
-        store_bf16(0, S, all_bf16, 0);
-        __syncthreads();
-        mfma_slice(0, false);
-        __syncthreads();
-        store_bf16(0, S, all_bf16, 1);
-        __syncthreads();
-        mfma_slice(0, false);
-        __syncthreads();
-    };
+    // slice of the r-th replay: the listed ones, then (if flagged) every
+    // slice from kMapSlices on; the next replay's loads are issued before
+    // the current one's MFMAs
     const int nlist = readfirstlane(redo_n);
-#pragma unroll 1
-    for (int r = 0; r < nlist; ++r) redo_slice(readfirstlane(redo[r]));
     const int late_end = readfirstlane(bad_map[kMapSlices] != 0ull ? 1 : 0) ? nslices : kMapSlices;
+    const int nreplay = nlist + max(late_end - kMapSlices, 0);
+    auto replay_slice = [&](int r) {
+        return r < nlist ? (int)readfirstlane(redo[r]) : kMapSlices + (r - nlist);
+    };
+    if (nreplay > 0) gload(replay_slice(0), S);
 #pragma unroll 1
-    for (int s = kMapSlices; s < late_end; ++s) redo_slice(s);
+    for (int r = 0; r < nreplay; ++r) {
+        store_bf16(0, S, all_bf16, 0);
+        store_weights(1, S, 128u, 0x07060302u);
+        __syncthreads();
+        gload(replay_slice(min(r + 1, nreplay - 1)), S);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            load_frag(0, 0, ks, F0);
+            mfma_frag(F0, false);
+            load_frag(0, 1, ks, F1);
+            mfma_frag(F1, false);
+        }
+        __syncthreads();
+    }
 
     // ---- epilogue: C[m][n] of tile (i, jn) in register r of lane l is
     // m = 8 (r / 4) + 4 (l / 32) + r % 4, n = l % 32
