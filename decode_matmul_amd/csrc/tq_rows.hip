@@ -32,6 +32,8 @@
 //    in distinct bank pairs.
 //  * Wave partials are kept per block in LDS and summed in a fixed order at
 //    the end, so results do not depend on timing.
+#include <algorithm>
+
 #include "common.h"
 
 namespace dmm {
@@ -41,7 +43,7 @@ namespace {
 constexpr int kW = 16;                  // waves per workgroup
 constexpr int kT = 64 * kW;             // threads per workgroup
 constexpr int kNB = 13;                 // code bytes per group of 64 trits
-constexpr int kNSB = 4;                 // blocks in flight
+constexpr int kNSB = 4;                 // blocks in flight (one block per thread slot)
 constexpr int kLutBytes = 256 * 256;    // entry b, copy c at (b << 8) | (c << 3)
 
 struct RowsParams {
@@ -58,6 +60,13 @@ struct RowsParams {
     int tile_bytes;          // one LDS tile: planes * 16 * (pitch + spitch)
     void* y;
     int y_dtype;
+    // grouped experts: workgroup w owns rows [c * rows_per_wg, ...) of expert
+    // w / chunks (c = w % chunks) for the token slots routed to it
+    const int32_t* ids;      // [T * top_k] expert of each (token, slot)
+    int total;               // T * top_k
+    int top_k;
+    int chunks;              // workgroups per expert
+    int64_t e_codes, e_scales;   // bytes per expert in a code / scale plane
 };
 
 __device__ __forceinline__ uint32_t trit_hi(int d) {     // bf16 high byte of 2t, d = t + 1
@@ -66,6 +75,7 @@ __device__ __forceinline__ uint32_t trit_hi(int d) {     // bf16 high byte of 2t
 
 // 16-byte chunk j of a block: where it comes from and where it goes.
 struct Chunk {
+    bool scale;              // a scale chunk (else codes)
     int64_t base;            // array offset from the plane-1 codes (codes or scales of one plane)
     int64_t row_bytes;       // bytes per row in that array
     int row;                 // row within the block
@@ -87,6 +97,7 @@ __device__ __forceinline__ Chunk chunk_of(const RowsParams& p, int j) {
     if (j < PL * cc) {
         const int pl = div(j, p.mul_cc), jj = j - pl * cc;
         const int r = div(jj, p.mul_cpr), k = jj - r * cpr;
+        c.scale = false;
         c.base = pl == 0 ? 0 : p.off_codes2;
         c.row_bytes = rb;
         c.row = r;
@@ -97,6 +108,7 @@ __device__ __forceinline__ Chunk chunk_of(const RowsParams& p, int j) {
         const int jj = j - PL * cc;
         const int pl = div(jj, p.mul_sc), js = jj - pl * sc;
         const int r = div(js, p.mul_spr), k = js - r * spr;
+        c.scale = true;
         c.base = pl == 0 ? p.off_scales1 : p.off_scales2;
         c.row_bytes = 2 * p.ng;
         c.row = r;
@@ -104,6 +116,7 @@ __device__ __forceinline__ Chunk chunk_of(const RowsParams& p, int j) {
         c.dst = PL * 16 * p.pitch + pl * 16 * p.spitch + r * p.spitch + 16 * k;
         c.valid = true;
     } else {
+        c.scale = false;
         c.base = 0;
         c.row_bytes = rb;
         c.row = 0;
@@ -114,7 +127,7 @@ __device__ __forceinline__ Chunk chunk_of(const RowsParams& p, int j) {
     return c;
 }
 
-template <int PL, int SPB>
+template <int PL, int SPB, bool GR>
 __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
@@ -124,23 +137,95 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
-    const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_wg;
+    // work item: the row range, and (grouped) the expert
+    const int e = GR ? (int)blockIdx.x / p.chunks : 0;
+    const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x - e * p.chunks : (int)blockIdx.x) * p.rows_per_wg;
     const int64_t r1 = min(r0 + (int64_t)p.rows_per_wg, p.N);
     const int64_t rlast = r1 - 1;
     const int nb = (int)((r1 - r0 + 15) >> 4);
 
-    // ---- activations of this wave's quad, block diagonal, zero elsewhere
+    // tokens: dense, rows 0 .. M-1 of x; grouped, the (token, slot) pairs
+    // routed to expert e, found by a wave-uniform scan of the ids
+    // Each wave scans the ids itself (64 per vector load, a ballot of the
+    // matches), so every wave holds the same uniform answer without a barrier.
+    // The k-th match is found from the ballot masks with scalar bit scans.
+    auto match_mask = [&](int i0) -> uint64_t {
+        const int i = i0 + lane;
+        const int v = i < p.total ? p.ids[i] : -1;
+        return __builtin_amdgcn_ballot_w64(v == e);
+    };
+    int ntok = p.M;
+    if constexpr (GR) {
+        ntok = 0;
+        for (int i0 = 0; i0 < p.total; i0 += 64) ntok += __builtin_popcountll(match_mask(i0));
+        if (ntok == 0) return;                   // whole workgroup: nothing routed here
+    }
+    const int npass = (ntok + 3) >> 2;
+
     const int col = lane & 15;
     const int kb = lane >> 4;
     const int nquads = p.ng >> 2;
     const bool quad_ok = wave < nquads;
     const int g = 4 * wave + kb;
-    // (loaded first so that masking them below waits for these loads only)
     const int ar = lane & 15;
-    const bool a_ok = (ar & 3) == kb && (ar >> 2) < p.M && quad_ok;
+    const uint32_t cofs = (uint32_t)col << 3;
+
+    // this thread's chunks of every block: byte offset (from p.base) in block
+    // 0, the offset of the same chunk in the last row of the range (rows past
+    // it are clamped onto it), the per-block step and the LDS destination
+    int64_t c_first[SPB], c_last[SPB];
+    int c_dst[SPB];
+    bool c_scale[SPB], c_valid[SPB];
+#pragma unroll
+    for (int s = 0; s < SPB; ++s) {
+        const Chunk c = chunk_of<PL>(p, s * kT + tid);
+        int64_t base = c.base;
+        if constexpr (GR) base += c.scale ? (int64_t)e * p.e_scales : (int64_t)e * p.e_codes;
+        c_first[s] = base + min(r0 + c.row, rlast) * c.row_bytes + c.col_bytes;
+        c_last[s] = base + rlast * c.row_bytes + c.col_bytes;
+        c_dst[s] = c.dst;
+        c_scale[s] = c.scale;
+        c_valid[s] = c.valid;
+    }
+    const int64_t step_codes = 16 * (int64_t)p.ng * kNB, step_scales = 32 * (int64_t)p.ng;
+    auto load = [&](int blk, u32x4 (&R)[SPB]) {
+        const int bc = min(blk, nb - 1);
+#pragma unroll
+        for (int s = 0; s < SPB; ++s) {
+            const int64_t off = min(c_first[s] + bc * (c_scale[s] ? step_scales : step_codes), c_last[s]);
+            R[s] = __builtin_nontemporal_load((const u32x4*)(p.base + off));
+        }
+    };
+
+  for (int pass = 0; pass < npass; ++pass) {
+    // the pass's tokens m < mt: activation row xr_m and output row or slot or_m
+    const int mt = min(4, ntok - 4 * pass);
+    int o0 = 4 * pass, o1 = 4 * pass + 1, o2 = 4 * pass + 2, o3 = 4 * pass + 3;
+    if constexpr (GR) {
+        int k = 0;                         // matches before the current 64 ids
+        for (int i0 = 0; i0 < p.total && k < 4 * pass + 4; i0 += 64) {
+            uint64_t m = match_mask(i0);
+            while (m != 0ull) {
+                const int q = k - 4 * pass;
+                const int i = i0 + (int)__builtin_ctzll(m);
+                if (q == 0) o0 = i;
+                else if (q == 1) o1 = i;
+                else if (q == 2) o2 = i;
+                else if (q == 3) o3 = i;
+                ++k;
+                m &= m - 1ull;
+            }
+        }
+    }
+    auto out_row = [&](int m) { return m == 0 ? o0 : (m == 1 ? o1 : (m == 2 ? o2 : o3)); };
+    auto x_row = [&](int m) { return GR ? out_row(m) / p.top_k : out_row(m); };
+
+    // ---- activations of this wave's quad, block diagonal, zero elsewhere
+    // (loaded first so that masking them below waits for these loads only)
+    const bool a_ok = (ar & 3) == kb && (ar >> 2) < mt && quad_ok;
     u32x4 A[8];
     {
-        const int mc = min(ar >> 2, p.M - 1);
+        const int mc = x_row(min(ar >> 2, mt - 1));
         const int gc = quad_ok ? g : 0;
         const uint16_t* xp = p.x + (int64_t)mc * p.K + (int64_t)gc * 64;
 #pragma unroll
@@ -148,26 +233,14 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);     // activations are issued before the code stream
 
-    // ---- this thread's chunks of every block, and the first kNSB blocks
-    Chunk ch[SPB];
+    // ---- the first NSB blocks (fewer in flight when a block takes two slots)
+    constexpr int NSB = SPB == 1 ? kNSB : kNSB - 1;
+    u32x4 R[NSB][SPB];
 #pragma unroll
-    for (int s = 0; s < SPB; ++s) ch[s] = chunk_of<PL>(p, s * kT + tid);
-    auto load = [&](int blk, u32x4 (&R)[SPB]) {
-        const int bc = min(blk, nb - 1);
-#pragma unroll
-        for (int s = 0; s < SPB; ++s) {
-            const int64_t row = min(r0 + 16 * bc + ch[s].row, rlast);
-            R[s] = __builtin_nontemporal_load(
-                (const u32x4*)(p.base + ch[s].base + row * ch[s].row_bytes + ch[s].col_bytes));
-        }
-    };
-    u32x4 R0[SPB], R1[SPB], R2[SPB], R3[SPB];
-    load(0, R0);
-    load(1, R1);
-    load(2, R2);
-    load(3, R3);
+    for (int d = 0; d < NSB; ++d) load(d, R[d]);
 
-    // ---- trit table, 16 copies
+    // ---- trit table, 16 copies (first pass; read only after the first barrier)
+    if (pass == 0)
     for (int i = tid; i < 256 * 16; i += kT) {
         const int b = i >> 4, c = i & 15;
         uint32_t lo = 0, hi = 0;
@@ -184,14 +257,13 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
 
 #pragma unroll
     for (int q = 0; q < 8; ++q) A[q] = a_ok ? A[q] : u32x4{0u, 0u, 0u, 0u};
-    const uint32_t cofs = (uint32_t)col << 3;
 
     auto store = [&](int buf, const u32x4 (&R)[SPB]) {
         unsigned char* t = tiles + buf * p.tile_bytes;
 #pragma unroll
         for (int s = 0; s < SPB; ++s) {
-            if (ch[s].valid) {
-                uint2* d = (uint2*)(t + ch[s].dst);
+            if (c_valid[s]) {
+                uint2* d = (uint2*)(t + c_dst[s]);
                 d[0] = make_uint2(R[s].x, R[s].y);
                 d[1] = make_uint2(R[s].z, R[s].w);
             }
@@ -215,32 +287,39 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
                 D[1] = align_bytes(W2, W1, sh);
                 D[2] = align_bytes(W3, W2, sh);
                 D[3] = align_bytes(0u, W3, sh);
+                // in two halves (trits 0..31 from bytes 0..6, trits 32..63 from
+                // bytes 6..12), each feeding four MFMAs, to bound the live words
                 uint32_t Elo[kNB], Ehi[kNB];
-#pragma unroll
-                for (int i = 0; i < kNB; ++i) {
-                    const uint32_t a = perm_b32(D[i >> 2], cofs, 0x0c0c0400u + ((uint32_t)(i & 3) << 8));
-                    const uint2 e = *(const uint2*)(lut + a);
-                    Elo[i] = e.x;
-                    Ehi[i] = e.y;
-                }
-                uint32_t B[32];
-#pragma unroll
-                for (int p2 = 0; p2 < 32; ++p2) {
-                    const int ja = 2 * p2, jb = 2 * p2 + 1;
-                    const int ia = ja / 5, qa = ja % 5, ib = jb / 5, qb = jb % 5;
-                    const uint32_t ra = qa < 4 ? Elo[ia] : Ehi[ia];
-                    const uint32_t rbv = qb < 4 ? Elo[ib] : Ehi[ib];
-                    const uint32_t ba = qa < 4 ? qa : 0, bb = qb < 4 ? qb : 0;
-                    const bool same = (ia == ib) && ((qa < 4) == (qb < 4));
-                    B[p2] = same ? perm_b32(ra, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | (bb << 24))
-                                 : perm_b32(rbv, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | ((4u + bb) << 24));
-                }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const u32x4 bq = {B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, A[q]), __builtin_bit_cast(bf16x8, bq), acc, 0, 0, 0);
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int i = half == 0 ? 0 : 7; i < (half == 0 ? 7 : kNB); ++i) {
+                        const uint32_t a = perm_b32(D[i >> 2], cofs, 0x0c0c0400u + ((uint32_t)(i & 3) << 8));
+                        const uint2 e2 = *(const uint2*)(lut + a);
+                        Elo[i] = e2.x;
+                        Ehi[i] = e2.y;
+                    }
+                    uint32_t B[16];
+#pragma unroll
+                    for (int p3 = 0; p3 < 16; ++p3) {
+                        const int p2 = 16 * half + p3;
+                        const int ja = 2 * p2, jb = 2 * p2 + 1;
+                        const int ia = ja / 5, qa = ja % 5, ib = jb / 5, qb = jb % 5;
+                        const uint32_t ra = qa < 4 ? Elo[ia] : Ehi[ia];
+                        const uint32_t rbv = qb < 4 ? Elo[ib] : Ehi[ib];
+                        const uint32_t ba = qa < 4 ? qa : 0, bb = qb < 4 ? qb : 0;
+                        const bool same = (ia == ib) && ((qa < 4) == (qb < 4));
+                        B[p3] = same ? perm_b32(ra, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | (bb << 24))
+                                     : perm_b32(rbv, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | ((4u + bb) << 24));
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const u32x4 bq = {B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]};
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, A[4 * half + q]), __builtin_bit_cast(bf16x8, bq),
+                            acc, 0, 0, 0);
+                    }
                 }
                 // scales of groups 4w .. 4w+3 of row col (C rows 4m + i)
                 const uint2 sw = *(const uint2*)(t + PL * 16 * p.pitch + pl * 16 * p.spitch +
@@ -256,22 +335,20 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         red[(blk * kW + wave) * 64 + lane] = part;
     };
 
-    // blocks b0 .. b0+3 sit in R0..R3; tile parity equals block parity
-    auto body = [&](int blk, u32x4 (&R)[SPB]) {
-        store(blk & 1, R);
+    // blocks b0 .. b0+NSB-1 sit in R[0..NSB-1]; tile parity equals block parity
+    auto body = [&](int blk, u32x4 (&Rb)[SPB]) {
+        store(blk & 1, Rb);
         __syncthreads();
-        load(blk + kNSB, R);
+        load(blk + NSB, Rb);
         if (blk < nb) compute(blk, blk & 1);
     };
-    for (int b0 = 0; b0 < nb; b0 += kNSB) {
-        body(b0, R0);
-        body(b0 + 1, R1);
-        body(b0 + 2, R2);
-        body(b0 + 3, R3);
+    for (int b0 = 0; b0 < nb; b0 += NSB) {
+#pragma unroll
+        for (int d = 0; d < NSB; ++d) body(b0 + d, R[d]);
     }
     __syncthreads();
 
-    // ---- fixed-order sum of the wave partials, then y
+    // ---- fixed-order sum of the wave partials, then y (grouped: row slot of y)
     for (int o = tid; o < nb * 64; o += kT) {
         const int blk = o >> 6, l = o & 63;
         const int m = l >> 4;
@@ -279,12 +356,14 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < kW; ++w) v += red[(blk * kW + w) * 64 + l];
-        if (m < p.M && n < r1) {
-            const int64_t idx = (int64_t)m * p.N + n;
+        if (m < mt && n < r1) {
+            const int64_t idx = (int64_t)out_row(m) * p.N + n;
             if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
             else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
         }
     }
+    __syncthreads();                       // the next pass reuses the tiles and partials
+  }
 }
 
 constexpr int kMaxBlocks = 8;
@@ -307,10 +386,13 @@ int compute_units() {
 }  // namespace
 
 // Streaming ternary GEMV; returns false (launching nothing) when the call is
-// outside its domain: dense, G = 64, 1 <= M <= 4, groups per row 16, 32, 48
-// or 64, 16-byte aligned operands, LDS within the limit.
+// outside its domain: G = 64, groups per row 16, 32, 48 or 64, 16-byte
+// aligned operands, LDS within the limit; dense calls with 1 <= M <= 4, or
+// grouped expert calls (any number of tokens per expert, in passes of four).
 bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
-    if (a.n_experts != 0 || a.G != 64 || a.M < 1 || a.M > 4 || a.N < 1) return false;
+    const bool grouped = a.n_experts > 0;
+    if (a.G != 64 || a.M < 1 || a.N < 1) return false;
+    if (!grouped && a.M > 4) return false;
     const int64_t ng = a.K / 64;
     if (a.K % 64 != 0 || ng < 16 || ng % 16 != 0 || ng > 64) return false;
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
@@ -321,7 +403,7 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.K = a.K;
     p.N = a.N;
     p.ng = (int)ng;
-    p.M = (int)a.M;
+    p.M = grouped ? 0 : (int)a.M;
     // byte distances between the operand arrays, so the kernel addresses all
     // four from one base without selecting pointers per lane
     auto dist = [&](const void* q) { return (int64_t)((intptr_t)q - (intptr_t)a.codes[0]); };
@@ -337,10 +419,15 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.pitch = (int)ng * kNB + 8;
     p.spitch = 2 * (int)ng + 8;
     p.tile_bytes = a.planes * 16 * (p.pitch + p.spitch);
-    const int cus = compute_units();
-    int64_t rpw = (a.N + cus - 1) / cus;
-    rpw = (rpw + 7) & ~(int64_t)7;
-    if (rpw > 16 * kMaxBlocks) rpw = 16 * kMaxBlocks;
+    int64_t rpw;
+    if (grouped) {
+        rpw = std::min<int64_t>(16 * kMaxBlocks, (a.N + 7) & ~(int64_t)7);
+    } else {
+        const int cus = compute_units();
+        rpw = (a.N + cus - 1) / cus;
+        rpw = (rpw + 7) & ~(int64_t)7;
+        if (rpw > 16 * kMaxBlocks) rpw = 16 * kMaxBlocks;
+    }
     p.rows_per_wg = (int)rpw;
     const int blocks = (int)((rpw + 15) / 16);
     const size_t smem = 2 * (size_t)p.tile_bytes + (size_t)blocks * kW * 64 * sizeof(float);
@@ -350,14 +437,28 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     if (spb > 2) return false;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
-    const dim3 grid((unsigned)((a.N + rpw - 1) / rpw)), block(kT);
+    p.ids = a.ids;
+    p.total = grouped ? (int)(a.M * a.top_k) : 0;
+    p.top_k = a.top_k;
+    p.chunks = (int)((a.N + rpw - 1) / rpw);
+    p.e_codes = a.N * ng * kNB;
+    p.e_scales = a.N * ng * 2;
+    const int64_t wgs = grouped ? (int64_t)a.n_experts * p.chunks : p.chunks;
+    if (wgs >= (1ll << 31)) return false;
+    const dim3 grid((unsigned)wgs), block(kT);
+#define DMM_ROWS(PL_, SPB_)                                                                \
+    do {                                                                                   \
+        if (grouped) hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, true>), grid, block, smem, s, p); \
+        else hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, false>), grid, block, smem, s, p); \
+    } while (0)
     if (a.planes == 1) {
-        if (spb == 1) hipLaunchKernelGGL((tq_rows_kernel<1, 1>), grid, block, smem, s, p);
-        else hipLaunchKernelGGL((tq_rows_kernel<1, 2>), grid, block, smem, s, p);
+        if (spb == 1) DMM_ROWS(1, 1);
+        else DMM_ROWS(1, 2);
     } else {
-        if (spb == 1) hipLaunchKernelGGL((tq_rows_kernel<2, 1>), grid, block, smem, s, p);
-        else hipLaunchKernelGGL((tq_rows_kernel<2, 2>), grid, block, smem, s, p);
+        if (spb == 1) DMM_ROWS(2, 1);
+        else DMM_ROWS(2, 2);
     }
+#undef DMM_ROWS
     *err = hipGetLastError();
     return true;
 }

@@ -332,6 +332,16 @@ def test_tq_matmul_grouped_small(dmm):
     grouped_case(dmm, 8, 40, 256, 6, 3, 2, seed=7, bad_ids=True)
 
 
+def test_tq_matmul_grouped_streaming(dmm):
+    """Grouped shapes of the streaming form (K = 1024 .. 4096): experts with
+    more than four routed slots (several passes), partial row ranges, tiny N,
+    out-of-range expert ids."""
+    grouped_case(dmm, 6, 100, 1024, 9, 3, 1, seed=21)
+    grouped_case(dmm, 4, 300, 2048, 16, 2, 2, seed=22)
+    grouped_case(dmm, 8, 64, 4096, 6, 3, 2, seed=23, bad_ids=True)
+    grouped_case(dmm, 3, 17, 3072, 2, 1, 1, seed=24)
+
+
 def test_tq_grouped_equals_dense_when_one_expert(dmm):
     """Every (token, slot) routed to expert 2 gives, slot by slot, exactly the
     dense result of expert 2's package (same kernel arithmetic)."""
