@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0
 # copy read and write 512 MiB), in profiles/hbm_traffic_rb_gemv_tq_rows.md.
 # The figure belongs to the kernel source it was measured on: any other
 # source of rb_gemv.hip reports null.
-MEASURED_TRAFFIC = {"rb_gemv.hip": ("6aba783a075bef5a", 67368885)}
+MEASURED_TRAFFIC = {"rb_gemv.hip": ("b9cc705c1f838449", 67343990)}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "packed matmul: weight GB/s vs HBM peak at M=1–16; TFLOP/s at M=2048"
 
@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--M", type=int, default=1, help="tokens of the headline GEMV")
     ap.add_argument("--layers", type=int, default=8, help="code matrices per step")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="warm-up continues untimed until this many seconds of work have run")
     ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads)")
     ap.add_argument("--extras", default="routeb,ternary,moe,prefill",
                     help="comma list of extra workloads to time (routeb, ternary, moe, prefill)")
@@ -118,11 +120,21 @@ class Timed:
         else:
             self.fn()
 
-    def time(self, reps, warmup):
+    def time(self, reps, warmup, settle_s=0.0):
+        """`warmup` untimed repetitions, continued (untimed) until `settle_s`
+        seconds of back-to-back work have passed: the GPU raises its clocks
+        over the first tenths of a second under load, and a few warm-up steps
+        of a ~0.15 ms step would otherwise time the ramp.  Then `reps` timed
+        repetitions."""
         torch = self.torch
+        t_start = time.perf_counter()
         for _ in range(warmup):
             self.run()
         torch.cuda.synchronize()
+        while time.perf_counter() - t_start < settle_s:
+            for _ in range(8):
+                self.run()
+            torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -220,7 +232,7 @@ def main():
     t.run()
     torch.cuda.synchronize()
     graph_ok = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, ys))
-    wall, gpu = t.time(args.steps, args.warmup)
+    wall, gpu = t.time(args.steps, args.warmup, args.settle_s)
 
     bytes_launch = N * K + 243 * 4 + M * K * 2 + M * N * 2
     per_launch = gpu / (args.steps * L)
@@ -245,6 +257,7 @@ def main():
                         f"fp32 layer scale, bf16 x at M={M}, bf16 y; {L} code matrices per step",
             "M": M, "N": N, "K": K, "layers_per_step": L,
             "graph": use_graph, "graph_matches_eager": bool(graph_ok),
+            "warmup_settle_s": args.settle_s,
         },
         "roofline": {
             "bound": "hbm",
@@ -276,9 +289,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _timed_launches(torch, fn, n_launch, use_graph, reps=20, warmup=3):
+def _timed_launches(torch, fn, n_launch, use_graph, reps=20, warmup=3, settle_s=0.2):
     t = Timed(torch, fn, use_graph)
-    wall, gpu = t.time(reps, warmup)
+    wall, gpu = t.time(reps, warmup, settle_s)
     return gpu / (reps * n_launch)
 
 

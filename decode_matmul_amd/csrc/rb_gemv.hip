@@ -7,22 +7,22 @@
 // applied to the accumulator before the bias).
 //
 // Mapping onto gfx950:
-//  * The workgroup (16 waves, one per CU: the replicated table fills LDS)
-//    owns 32 output rows; its waves split K into contiguous ranges, each
-//    wave streams both 16-row blocks with loads two steps ahead of the
-//    MFMAs, and the partials meet in LDS at the end (fixed summation order).
+//  * General path: the workgroup (16 waves, one per CU: the replicated table
+//    fills LDS) owns 32 output rows; its waves split K into contiguous
+//    ranges, each wave streams both 16-row blocks with loads two steps ahead
+//    of the MFMAs, and the partials meet in LDS at the end (fixed summation
+//    order).  Tiled path (K % 512 == 0): see rb_gemv_tiled_kernel.
 //  * Each code byte is looked up in an LDS copy of the code book.  Every
 //    fp32 entry v is stored as two bf16 terms, hi = bf16(v) and
 //    lo = bf16(v - hi) (|v - hi - lo| <= 2^-17 |v|), packed as one dword.
-//    The table is replicated 64 times with entry b of copy c at byte
-//    256 b + 4 c, so lane c always hits its own bank and the address is a
-//    single v_perm of the code dword with the lane offset.
+//    The table is replicated (64 copies in the general path, entry b of copy
+//    c at byte 256 b + 4 c; 16 in the tiled path) so that the lanes reading
+//    at once mostly hit distinct banks, and the address is a single v_perm
+//    of the code dword with the lane offset.
 //  * bf16 MFMA 16x16x32: B takes the looked-up (hi, lo) dword as two K-slots
 //    of one weight, A holds the activation twice in the same two slots, so
 //    one MFMA accumulates x*hi + x*lo = x*v for four weights per lane.
 //    A rows are the M <= 16 tokens; C columns are the 16 rows.
-//  * Each lane streams 16 consecutive code bytes of one row per step
-//    (16 B loads; 4 lanes cover 64 contiguous bytes of a row).
 #include "common.h"
 
 namespace dmm {
@@ -32,12 +32,15 @@ namespace {
 constexpr int kWaves = 16;                // K split over the waves of a workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRB = 2;                    // 16-row blocks per workgroup, all streamed by each wave
-constexpr int kTileRows = 16 * kRB;       // tiled path: rows per workgroup
-constexpr int kTileK = 1024;              // tiled path: K bytes per tile (64 per wave)
-constexpr int kTilePitch = kTileK + 16;   // padded LDS row pitch: column reads hit distinct banks
-static_assert(kTileK == 64 * kWaves, "one 64-column slice per wave");
-static_assert(kTileRows == 2 * kWaves, "two rows fetched per wave");
-static_assert(kTileRows * kTilePitch >= kWaves * kRB * 64 * 4 * 4, "reduction fits the tile");
+// tiled path: 8 waves on 16 rows; a tile is 16 rows x 512 code bytes, each
+// wave fetches two of its rows and reads back a 64-column slice of all 16
+constexpr int kTWaves = 8;
+constexpr int kTThreads = 64 * kTWaves;
+constexpr int kTileK = 64 * kTWaves;        // K bytes per tile
+constexpr int kTilePitch = kTileK + 16;     // padded LDS row pitch: column reads hit distinct banks
+constexpr int kTileBytes = 16 * kTilePitch;
+constexpr int kTCopies = 16;                // code-book copies in the tiled path
+static_assert(2 * kTileBytes >= kTWaves * 64 * 4 * 4, "reduction fits the tile buffers");
 constexpr int kLutBytes = 256 * 256;       // 256 entries x 64 copies x 4 B
 
 struct Params {
@@ -303,31 +306,29 @@ rb_gemv_kernel(Params p) {
     }
 }
 
-// Fast path: codes 16-byte aligned, K % 1024 == 0, x 4-byte aligned.
+// Fast path: codes 16-byte aligned, K % 512 == 0, x 4-byte aligned.
 //
-// The workgroup (16 waves) owns 32 rows.  K is walked in tiles of 32 rows x
-// 1 KB: each wave fetches two rows of the tile with one 1 KB load per row
-// (every load instruction covers 1 KB of one row, the pattern HBM streams
-// best), two tiles ahead in registers; the tile is written to LDS and each
-// wave then reads its 64-column slice of all 32 rows in the MFMA layout.
-__global__ void __launch_bounds__(kThreads)
+// The workgroup (8 waves, up to four per CU) owns 16 rows.  K is walked in
+// tiles of 16 rows x 512 bytes: each wave fetches two rows of the tile (32
+// lanes x 16 B per row), two tiles ahead in registers; the tile goes to one of
+// two LDS buffers and each wave then reads its 64-column slice of all 16 rows
+// in the MFMA layout, one barrier per tile.  Small workgroups with a small
+// code-book copy (16 copies, 16 KB) let several workgroups share a CU, so one
+// waiting at its barrier leaves the others streaming.
+__global__ void __launch_bounds__(kTThreads, 2)
 rb_gemv_tiled_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char tile[kTileRows * kTilePitch];
+    __shared__ __attribute__((aligned(16))) unsigned char lut[256 * 4 * kTCopies];
+    __shared__ __attribute__((aligned(16))) unsigned char tiles[2][kTileBytes];
 
     const int tid = threadIdx.x;
     const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
-    const int64_t row0 = (int64_t)blockIdx.x * kTileRows;
+    const int64_t row0 = (int64_t)blockIdx.x * 16;
     const int64_t ntiles = p.K / kTileK;          // >= 1: the launcher requires K >= kTileK
 
-    // rows this wave fetches: 2 * wave, 2 * wave + 1 (clamped into range)
-    const uint8_t* grow[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t r = min(row0 + 2 * wave + i, p.N - 1);
-        grow[i] = p.codes + r * p.K + 16 * lane;
-    }
+    // tile row this lane fetches (clamped into range), 16 bytes at 16 (lane & 31)
+    const int lrow = 2 * wave + (lane >> 5);
+    const uint8_t* grow = p.codes + min(row0 + lrow, p.N - 1) * p.K + 16 * (lane & 31);
     // activations of this wave's slice: token (lane & 15), 16 columns
     const int am = lane & 15;
     const bool a_ok = am < p.M;
@@ -336,13 +337,12 @@ rb_gemv_tiled_kernel(Params p) {
     const uint16_t* xrow = p.x + (a_ok ? am : 0) * p.K + 64 * wave + 16 * kb;
 
     struct Stage {
-        u32x4a c[2];
+        u32x4a c;
         uint32_t X[8];
     };
     auto fetch = [&](int64_t t, Stage& S) {
         const int64_t tc = min(t, ntiles - 1);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) S.c[i] = *(const u32x4a*)(grow[i] + tc * kTileK);
+        S.c = *(const u32x4a*)(grow + tc * kTileK);
         const u32x4a* xp = (const u32x4a*)(xrow + tc * kTileK);
         u32x4a a = xp[0], b = xp[1];
         S.X[0] = a.x; S.X[1] = a.y; S.X[2] = a.z; S.X[3] = a.w;
@@ -351,42 +351,36 @@ rb_gemv_tiled_kernel(Params p) {
 
     // the code-book read goes first so that waiting for it leaves the tile
     // loads in flight (memory counters complete in order)
-    const int lb = tid >> 2;
+    const int lb = tid >> 1;
     const float tv = p.table[lb < 243 ? lb : 0];
     Stage s0, s1;
     fetch(0, s0);
     fetch(1, s1);
 
-    {   // entry b, copies 16 (tid & 3) .. + 15
-        const int b = lb;
-        const uint32_t e = split_entry(b < 243 ? tv : 0.f);
+    {   // entry b, copies 8 (tid & 1) .. + 7; entries 243..255 read zero
+        const uint32_t e = split_entry(lb < 243 ? tv : 0.f);
         const u32x4 q = {e, e, e, e};
-        unsigned char* base = lut + b * 256 + (tid & 3) * 64;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(base + 16 * i) = q;
+        unsigned char* base = lut + lb * 4 * kTCopies + (tid & 1) * 2 * kTCopies;
+        *(u32x4*)base = q;
+        *(u32x4*)(base + 16) = q;
     }
 
-    f32x4 acc[kRB];
-#pragma unroll
-    for (int r = 0; r < kRB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint32_t lane_off = (uint32_t)lane << 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // entry b, copy c at byte 64 b + 4 c; lane l reads copy l % 16: the
+    // v_perm below forms 256 b + 16 (l % 16), shifted right by two
+    const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
 
-    auto step = [&](const Stage& S) {
-        __syncthreads();                                  // tile free again
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            *(u32x4*)(tile + (2 * wave + i) * kTilePitch + 16 * lane) =
-                u32x4{S.c[i].x, S.c[i].y, S.c[i].z, S.c[i].w};
+    // tile t goes to LDS buffer t & 1: the barrier after writing tile t also
+    // orders every read of tile t - 2 (same buffer) before its overwrite
+    auto step = [&](const Stage& S, int buf) {
+        unsigned char* tile = tiles[buf];
+        *(u32x4*)(tile + lrow * kTilePitch + 16 * (lane & 31)) = u32x4{S.c.x, S.c.y, S.c.z, S.c.w};
         __syncthreads();
-        uint32_t D[kRB][4];
-#pragma unroll
-        for (int r = 0; r < kRB; ++r) {
-            u32x4 v = *(const u32x4*)(tile + (16 * r + col) * kTilePitch + 64 * wave + 16 * kb);
-            D[r][0] = v.x; D[r][1] = v.y; D[r][2] = v.z; D[r][3] = v.w;
-        }
+        const u32x4 v = *(const u32x4*)(tile + col * kTilePitch + 64 * wave + 16 * kb);
+        const uint32_t D[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            u32x4 aq;
+            u32x4 aq, bq;
             // lanes of tokens >= M hold token 0's activations: they only feed
             // rows of C that are never stored
             const uint32_t x01 = S.X[2 * j], x23 = S.X[2 * j + 1];
@@ -395,41 +389,34 @@ rb_gemv_tiled_kernel(Params p) {
             aq[2] = perm_b32(x23, x23, 0x01000100u);
             aq[3] = perm_b32(x23, x23, 0x03020302u);
 #pragma unroll
-            for (int r = 0; r < kRB; ++r) {
-                u32x4 bq;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t addr =
-                        perm_b32(D[r][j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8));
-                    bq[i] = *(const uint32_t*)(lut + addr);
-                }
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, aq), __builtin_bit_cast(bf16x8, bq), acc[r], 0,
-                    0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t addr =
+                    perm_b32(D[j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8)) >> 2;
+                bq[i] = *(const uint32_t*)(lut + addr);
             }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aq),
+                                                          __builtin_bit_cast(bf16x8, bq), acc,
+                                                          0, 0, 0);
         }
     };
 
     int64_t t = 0;
     for (; t + 1 < ntiles; t += 2) {
-        step(s0);
+        step(s0, 0);
         fetch(t + 2, s0);
-        step(s1);
+        step(s1, 1);
         fetch(t + 3, s1);
     }
-    if (t < ntiles) step(s0);
+    if (t < ntiles) step(s0, 0);
 
-    // partials of the 16 waves meet in the (now idle) tile buffer
+    // partials of the 8 waves meet in the (now idle) tile buffers
     __syncthreads();
-    float* red = (float*)tile;                                    // [kWaves][kRB][64][4]
+    float* red = (float*)tiles[0];                                // [kTWaves][64][4]
 #pragma unroll
-    for (int r = 0; r < kRB; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[((wave * kRB + r) * 64 + lane) * 4 + i] = acc[r][i];
+    for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
     __syncthreads();
-    if (wave < kRB) {
-        const int r = wave;
-        const int64_t n = row0 + 16 * r + col;
+    if (wave == 0) {
+        const int64_t n = row0 + col;
         if (n < p.N) {
             const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
             const float bias = p.bias ? p.bias[n] : 0.f;
@@ -437,8 +424,8 @@ rb_gemv_tiled_kernel(Params p) {
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * kb + i;
                 if (m >= p.M) continue;
-                float v = red[(r * 64 + lane) * 4 + i];
-                for (int w = 1; w < kWaves; ++w) v += red[((w * kRB + r) * 64 + lane) * 4 + i];
+                float v = red[lane * 4 + i];
+                for (int w = 1; w < kTWaves; ++w) v += red[(w * 64 + lane) * 4 + i];
                 v = v * rho;
                 v = v * p.alpha;
                 v = v + bias;
@@ -478,7 +465,8 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
     const bool tiled = a.K >= kTileK && (a.K % kTileK == 0) &&
                        (((uintptr_t)a.codes & 15) == 0) && (((uintptr_t)a.x & 3) == 0);
     if (tiled) {
-        hipLaunchKernelGGL(rb_gemv_tiled_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(rb_gemv_tiled_kernel, dim3((unsigned)((a.N + 15) / 16)),
+                           dim3(kTThreads), 0, s, p);
         return hipGetLastError();
     }
     const bool aligned4 = (((uintptr_t)a.codes & 3) == 0) && (a.K % 4 == 0);

@@ -426,6 +426,21 @@ def test_rb_matmul_small(dmm, M, N, K):
     rb_case(dmm, M, N, K, seed=M + N + K, ydt=torch.bfloat16, rho=True, bias=True)
 
 
+# Shapes of the tiled GEMV form (K % 512 == 0, aligned operands): a single
+# tile, an odd number of tiles, ragged N (partial last 16-row block), N < 16,
+# every M up to 16, and code 250 (a zero entry) mixed in.
+RB_TILED_CASES = [
+    (1, 16, 512), (16, 17, 512), (3, 1000, 1536), (7, 33, 2560), (16, 4100, 1024),
+    (2, 1, 3584), (12, 250, 5120), (1, 3, 512),
+]
+
+
+@pytest.mark.parametrize("M,N,K", RB_TILED_CASES)
+def test_rb_matmul_tiled_shapes(dmm, M, N, K):
+    rb_case(dmm, M, N, K, seed=M * 11 + N + K, bad_codes=True)
+    rb_case(dmm, M, N, K, seed=M + 5 * N + K, ydt=torch.bfloat16, rho=True, bias=True)
+
+
 @pytest.mark.parametrize("code_off,x_off", [(1, 1), (2, 0), (3, 3)])
 def test_rb_matmul_offsets_and_bad_codes(dmm, code_off, x_off):
     rb_case(dmm, 4, 50, 256, 31, code_off=code_off, x_off=x_off, bad_codes=True)
