@@ -389,15 +389,16 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
     const int experts = p.grouped ? a.n_experts : 1;
     const int64_t items = (int64_t)p.row_blocks * experts;
     if (items == 0) return hipSuccess;
+    {
+        // the streaming form writes the rows of out-of-range expert ids itself
+        hipError_t e;
+        if (launch_tq_rows(a, s, &e)) return e;
+    }
     if (p.grouped) {
         // slots routed to no valid expert: NaN rows (no expert kernel writes them)
         const int total = (int)(a.M * a.top_k);
         hipLaunchKernelGGL(bad_ids_kernel, dim3(total), dim3(256), 0, s, a.ids, total,
                            a.n_experts, a.N, a.y, a.y_dtype);
-    }
-    {
-        hipError_t e;
-        if (launch_tq_rows(a, s, &e)) return e;
     }
     // activations staged in LDS when a chunk of <= 4 tokens fits comfortably
     const int64_t xlds_bytes = 4 * a.K * 2;

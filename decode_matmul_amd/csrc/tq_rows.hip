@@ -66,6 +66,8 @@ struct RowsParams {
     int total;               // T * top_k
     int top_k;
     int chunks;              // workgroups per expert
+    int n_experts;           // the workgroup after the last expert's writes the
+                             // NaN rows of slots routed to no valid expert
     int64_t e_codes, e_scales;   // bytes per expert in a code / scale plane
 };
 
@@ -137,6 +139,21 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
+    if constexpr (GR) {
+        if ((int)blockIdx.x == p.n_experts * p.chunks) {
+            // slots whose expert id is out of range: NaN rows
+            for (int i = 0; i < p.total; ++i) {
+                const int ei = p.ids[i];
+                if (ei >= 0 && ei < p.n_experts) continue;
+                for (int64_t n = tid; n < p.N; n += kT) {
+                    const int64_t o = (int64_t)i * p.N + n;
+                    if (p.y_dtype == TQ_F32) ((float*)p.y)[o] = __builtin_nanf("");
+                    else ((uint16_t*)p.y)[o] = 0x7fc0u;
+                }
+            }
+            return;
+        }
+    }
     // work item: the row range, and (grouped) the expert
     const int e = GR ? (int)blockIdx.x / p.chunks : 0;
     const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x - e * p.chunks : (int)blockIdx.x) * p.rows_per_wg;
@@ -441,9 +458,11 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.total = grouped ? (int)(a.M * a.top_k) : 0;
     p.top_k = a.top_k;
     p.chunks = (int)((a.N + rpw - 1) / rpw);
+    p.n_experts = grouped ? a.n_experts : 0;
     p.e_codes = a.N * ng * kNB;
     p.e_scales = a.N * ng * 2;
-    const int64_t wgs = grouped ? (int64_t)a.n_experts * p.chunks : p.chunks;
+    // grouped: one more workgroup for the slots routed to no valid expert
+    const int64_t wgs = grouped ? (int64_t)a.n_experts * p.chunks + 1 : p.chunks;
     if (wgs >= (1ll << 31)) return false;
     const dim3 grid((unsigned)wgs), block(kT);
 #define DMM_ROWS(PL_, SPB_)                                                                \

@@ -295,12 +295,14 @@ def test_tq_matmul_ternary_small_full(dmm):
     assert_bound(y_host(y), y_ref, B, "ternary_small")
 
 
-def grouped_case(dmm, E, N, K, T, top_k, planes, seed, bad_ids=False):
+def grouped_case(dmm, E, N, K, T, top_k, planes, seed, bad_ids=False, ydt=torch.float32):
     rng = np.random.default_rng(seed)
     W = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
     xb = workloads.bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
     ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.int32)
-    if bad_ids:
+    if bad_ids == "all":
+        ids[:] = np.where(np.arange(ids.size).reshape(ids.shape) % 2 == 0, -7, E + 3)
+    elif bad_ids:
         ids[1, 0] = E
         ids[2, top_k - 1] = -1
     if planes == 2:
@@ -308,8 +310,8 @@ def grouped_case(dmm, E, N, K, T, top_k, planes, seed, bad_ids=False):
     else:
         c1, s1 = oracle.quantize_pack(W.reshape(-1, K), 64)
         c2 = s2 = None
-    y = torch.empty((T, top_k, N), dtype=torch.float32, device=DEV)
-    say(f"tq_matmul grouped E={E} N={N} K={K} T={T} top_k={top_k} planes={planes} bad={bad_ids}")
+    y = torch.empty((T, top_k, N), dtype=ydt, device=DEV)
+    say(f"tq_matmul grouped E={E} N={N} K={K} T={T} top_k={top_k} planes={planes} bad={bad_ids} y={ydt}")
     dmm.tq_matmul(dev(bits16(xb)), dev(c1), dev(bits16(s1)), N, 64, y,
                   None if c2 is None else dev(c2), None if s2 is None else dev(bits16(s2)),
                   n_experts=E, expert_ids=dev(ids), top_k=top_k)
@@ -322,7 +324,8 @@ def grouped_case(dmm, E, N, K, T, top_k, planes, seed, bad_ids=False):
     valid = (ids >= 0) & (ids < E)
     ids_ok = np.where(valid, ids, 0)
     y_ref, B = oracle.grouped_ref(xb, ids_ok, w_of)
-    assert_bound(got[valid], y_ref[valid], B[valid], "grouped")
+    if valid.any():
+        assert_bound(got[valid], y_ref[valid], B[valid], "grouped", stored_of(y))
     assert np.all(np.isnan(got[~valid]))
 
 
@@ -330,6 +333,7 @@ def test_tq_matmul_grouped_small(dmm):
     grouped_case(dmm, 8, 40, 256, 6, 3, 2, seed=5)
     grouped_case(dmm, 5, 33, 128, 9, 2, 1, seed=6)
     grouped_case(dmm, 8, 40, 256, 6, 3, 2, seed=7, bad_ids=True)
+    grouped_case(dmm, 5, 33, 128, 4, 2, 1, seed=8, bad_ids="all", ydt=torch.bfloat16)
 
 
 def test_tq_matmul_grouped_streaming(dmm):
@@ -340,6 +344,8 @@ def test_tq_matmul_grouped_streaming(dmm):
     grouped_case(dmm, 4, 300, 2048, 16, 2, 2, seed=22)
     grouped_case(dmm, 8, 64, 4096, 6, 3, 2, seed=23, bad_ids=True)
     grouped_case(dmm, 3, 17, 3072, 2, 1, 1, seed=24)
+    grouped_case(dmm, 4, 40, 1024, 5, 2, 2, seed=25, bad_ids=True, ydt=torch.bfloat16)
+    grouped_case(dmm, 4, 40, 1024, 3, 2, 1, seed=26, bad_ids="all")
 
 
 def test_tq_grouped_equals_dense_when_one_expert(dmm):
