@@ -23,11 +23,33 @@ Readings taken where the page is silent:
 * alpha (fp32) and rho_n (fp16) are separate inputs; the weight is the
   float64 product alpha * T[b] * rho_n.
 * Bytes 243..255 are not code words: the table is padded with zeros to 256.
+
+The encoder (rb_encode) follows section 3.1 (the greedy 5-step word: each
+step picks the c in {-1, 0, +1} closest to the residual, then subtracts
+c * s_i; r_0 = x / alpha with alpha the largest |W| of the matrix; a zero-bias
+zeta forces c_i = 0 while |r_{i-1}| < zeta * s_i) and section 3.3 (per-row
+scale: r_0 = W[n, k] / alpha_n with alpha_n the row's largest |W|, and
+rho_n = alpha_n / alpha stored in fp16).  Readings where the page is silent:
+
+* The steps run in float64: r_0 is the float64 quotient of the fp32 weight
+  by the fp32 scale (one rounding), each residual r - c * s_i is rounded once
+  (c * s_i is exact), and the distances |r - s_i|, |r|, |r + s_i| and
+  zeta * s_i are float64 values.  A quantized code therefore depends only on
+  IEEE float64 operations, which any implementation reproduces bit for bit.
+* Ties in the argmin go to c = 0 (the value the zero-bias favours); a tie
+  between -1 and +1 cannot occur unless r = 0 or s_i = 0, where 0 wins too.
+* The zero-bias test is strict (|r| < zeta * s_i), zeta defaults to 0, and
+  with zeta <= 1/2 it never changes a word (the argmin already picks 0 there).
+* A zero scale (an all-zero row, or an all-zero matrix) gives r_0 = 0, hence
+  the all-zero word (code 121) for every weight, and rho_n = 0.
+* rho_n is the float64 quotient alpha_n / alpha rounded once to fp16
+  (nearest-even); alpha itself is returned as the fp32 value max |W|.
+* Non-finite weights are an error (the scale would not be defined).
 """
 
 import numpy as np
 
-from .fpround import f16_bits_to_f64, f64_to_f32
+from .fpround import f16_bits_to_f64, f64_to_f16_bits, f64_to_f32
 
 
 def code_words():
@@ -59,3 +81,45 @@ def rb_weights(codes, table, alpha, row_scale_bits=None):
         rho = f16_bits_to_f64(row_scale_bits)
         w = w * rho[:, None]
     return w
+
+
+def rb_encode(W, ladder, zeta=0.0, per_row=False):
+    """Route B encoder: W float32 [N, K] -> (codes uint8 [N, K], alpha float32,
+    rho fp16 bits uint16 [N] or None).  Section 3.1 steps, section 3.3 scales."""
+    W = np.asarray(W, dtype=np.float32)
+    if W.ndim != 2:
+        raise ValueError("W is a matrix")
+    if not np.all(np.isfinite(W)):
+        raise ValueError("non-finite weight")
+    s = np.asarray(ladder, dtype=np.float32).astype(np.float64)
+    if s.shape != (5,):
+        raise ValueError("the ladder has five steps")
+    a = np.abs(W.astype(np.float64))
+    alpha = float(a.max()) if W.size else 0.0            # max |W|: an fp32 value
+    N, K = W.shape
+    if per_row:
+        scale = a.max(axis=1) if K else np.zeros(N)        # alpha_n
+    else:
+        scale = np.full(N, alpha)
+    r = np.zeros((N, K), dtype=np.float64)
+    pos = scale > 0
+    r[pos] = W[pos].astype(np.float64) / scale[pos][:, None]
+    z = np.float64(np.float32(zeta))
+    codes = np.zeros((N, K), dtype=np.int64)
+    for i in range(5):                                     # c_1 .. c_5
+        d_zero = np.abs(r)
+        d_plus = np.abs(r - s[i])
+        d_minus = np.abs(r + s[i])
+        c = np.zeros((N, K), dtype=np.int64)
+        c[(d_plus < d_zero) & (d_plus < d_minus)] = 1
+        c[(d_minus < d_zero) & (d_minus < d_plus)] = -1
+        c[d_zero < z * s[i]] = 0                           # zero-bias
+        r = r - c * s[i]
+        codes = codes * 3 + (c + 1)                        # c_1 most significant
+    rho = None
+    if per_row:
+        q = np.zeros(N, dtype=np.float64)
+        if alpha > 0:
+            q = scale / alpha
+        rho = f64_to_f16_bits(q)
+    return codes.astype(np.uint8), np.float32(alpha), rho

@@ -565,3 +565,133 @@ def test_check_bound_bf16_allowance():
     assert oracle.check_bound(yr + 0.0035, yr, B, stored="bf16")["ok"]
     assert not oracle.check_bound(yr + 0.0035, yr, B)["ok"]
     assert not oracle.check_bound(yr + 0.0075, yr, B, stored="bf16")["ok"]
+
+
+# ---------------------------------------------------------- Route B encoder
+
+def _balanced_ternary(n, digits=5):
+    """Digits (most significant first) of the integer n in balanced ternary,
+    by repeated division with remainders in {-1, 0, 1}."""
+    out = []
+    for _ in range(digits):
+        r = n % 3
+        if r == 2:
+            r = -1
+        out.append(r)
+        n = (n - r) // 3
+    assert n == 0
+    return out[::-1]
+
+
+def test_encode_worked_examples():
+    """Hand-worked words of tests/golden/routeb_encode_example.txt (Route B,
+    sections 3.1 and 3.2), including the tie at |r| = s_1 / 2 and the strict
+    zero-bias test."""
+    lad = _ladders()["S0"]
+    W = np.array([[0.9, -0.5, 1.0, 0.0]], np.float32)
+    for ln in _golden_lines("routeb_encode_example.txt"):
+        x, zeta = float(ln[0]), float(ln[1])
+        word, code = [int(v) for v in ln[2:7]], int(ln[7])
+        assert sum((c + 1) * 3 ** (4 - i) for i, c in enumerate(word)) == code
+        codes, alpha, rho = oracle.rb_encode(W, lad, zeta=zeta)
+        assert alpha == np.float32(1.0) and rho is None
+        k = int(np.flatnonzero(W[0] == np.float32(x))[0])
+        assert int(codes[0, k]) == code, (x, zeta)
+        assert list(oracle.code_words()[code]) == word
+
+
+def test_encode_balanced_ladder_is_nearest_multiple_of_one_81st():
+    """With S0 = (1, 1/3, 1/9, 1/27, 1/81) the greedy word of r in [-1, 1] is
+    the balanced-ternary spelling of round(81 r) (away from the half-way
+    points, where the fp32 ladder and float64 rounding may tip a step)."""
+    lad = _ladders()["S0"]
+    rng = np.random.default_rng(3)
+    r = rng.uniform(-1, 1, 4000).astype(np.float32)
+    r[0] = 1.0                                           # alpha = 1 exactly
+    codes, alpha, _ = oracle.rb_encode(r[None, :], lad)
+    assert alpha == 1.0
+    cw = oracle.code_words()
+    checked = 0
+    for k in range(r.size):
+        t = 81.0 * float(r[k])
+        if abs(t - math.floor(t) - 0.5) < 1e-4:
+            continue
+        n = int(math.floor(t + 0.5))
+        assert list(cw[codes[0, k]]) == _balanced_ternary(n), (r[k], n)
+        checked += 1
+    assert checked > 3900
+
+
+def test_encode_greedy_residual_bound_and_decode():
+    """Balanced ladder: every |r_0| <= 1 is reconstructed to within s_5 / 2
+    (plus rounding), and alpha * T[code] is the decoded weight of section 3.2."""
+    lad = _ladders()["S0"]
+    rng = np.random.default_rng(4)
+    W = (rng.standard_normal((7, 300)) * 0.02).astype(np.float32)
+    codes, alpha, _ = oracle.rb_encode(W, lad)
+    assert alpha == np.abs(W).max()
+    T = oracle.rb_table(lad).astype(np.float64)
+    r0 = W.astype(np.float64) / float(alpha)
+    assert np.all(np.abs(r0 - T[codes]) <= 0.5 / 81 + 1e-7)
+    w_hat = oracle.rb_weights(codes, oracle.rb_table(lad), alpha)
+    assert np.all(np.abs(W - w_hat) <= float(alpha) * (0.5 / 81 + 1e-7))
+
+
+def test_encode_per_row_scale():
+    """Section 3.3: r_0 = W / alpha_n, so each row's largest |W| spells
+    (+-1, 0, 0, 0, 0) (codes 202 and 40 under S0); rho_n = fp16(alpha_n /
+    alpha) against numpy's float64 -> float16 rounding; alpha = max |W|."""
+    lad = _ladders()["S0"]
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((9, 70)) * rng.uniform(0.01, 1.0, (9, 1))).astype(np.float32)
+    W[3, 5] = -np.abs(W[3]).max() * 1.5                  # a negative row maximum
+    codes, alpha, rho = oracle.rb_encode(W, lad, per_row=True)
+    a_n = np.abs(W).max(axis=1)
+    assert alpha == np.abs(W).max()
+    for n in range(W.shape[0]):
+        k = int(np.argmax(np.abs(W[n])))
+        assert int(codes[n, k]) == (202 if W[n, k] > 0 else 40)
+    want = (a_n.astype(np.float64) / float(alpha)).astype(np.float16).view(np.uint16)
+    assert np.array_equal(rho, want)
+    # the row-normalised words equal the global encoding of W / alpha_n
+    for n in range(W.shape[0]):
+        row = (W[n].astype(np.float64) / float(a_n[n])).astype(np.float32)
+        c_row, _, _ = oracle.rb_encode(row[None, :], lad)
+        exact = np.all(W[n].astype(np.float64) / float(a_n[n]) == row.astype(np.float64))
+        if exact:
+            assert np.array_equal(c_row[0], codes[n])
+
+
+def test_encode_zero_scale_and_errors():
+    """Zero rows (and an all-zero matrix) give the all-zero word 121 and
+    rho = 0; non-finite weights are rejected."""
+    lad = _ladders()["S"]
+    W = np.zeros((3, 10), np.float32)
+    W[1, 2] = 0.5
+    codes, alpha, rho = oracle.rb_encode(W, lad, per_row=True)
+    assert alpha == 0.5
+    assert np.all(codes[[0, 2]] == 121) and rho[0] == 0 and rho[2] == 0
+    assert rho[1] == np.float16(1.0).view(np.uint16)
+    codes, alpha, _ = oracle.rb_encode(np.zeros((2, 4), np.float32), lad)
+    assert alpha == 0 and np.all(codes == 121)
+    for bad in (np.nan, np.inf, -np.inf):
+        W2 = W.copy()
+        W2[0, 0] = bad
+        with pytest.raises(ValueError):
+            oracle.rb_encode(W2, lad)
+
+
+def test_encode_zero_bias_below_one_half_changes_nothing():
+    """|r| < s/2 already makes 0 the nearest step, so a zero-bias zeta <= 1/2
+    leaves every word unchanged, while zeta = 1 only ever turns steps to 0
+    where |r| < s_i."""
+    lad = _ladders()["S"]
+    rng = np.random.default_rng(6)
+    W = rng.standard_normal((5, 400)).astype(np.float32)
+    c0, _, _ = oracle.rb_encode(W, lad)
+    for z in (0.1, 0.25, 0.5):
+        cz, _, _ = oracle.rb_encode(W, lad, zeta=z)
+        assert np.array_equal(c0, cz)
+    c1, _, _ = oracle.rb_encode(W, lad, zeta=1.0)
+    w0, w1 = oracle.code_words()[c0], oracle.code_words()[c1]
+    assert np.count_nonzero(w1) < np.count_nonzero(w0)
