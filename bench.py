@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="warm-up continues untimed until this many seconds of work have run")
     ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads)")
-    ap.add_argument("--extras", default="routeb,ternary,moe,prefill",
-                    help="comma list of extra workloads to time (routeb, ternary, moe, prefill)")
+    ap.add_argument("--extras", default="routeb,ternary,moe,encode,prefill",
+                    help="comma list of extra workloads to time "
+                         "(routeb, ternary, moe, encode, prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -370,6 +371,30 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         rec["touched_experts"] = touched
         res["moe_two_plane_T16"] = rec
         del pk
+
+    if "encode" in sel:
+        progress("extra: routeb_encode")
+        # Route B encoder with per-row scales, W fp32 8192 x 8192
+        d = workloads.routeb_encode()
+        N, K = d["W"].shape
+        W = to_dev(d["W"])
+        codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+        rs = torch.empty(N, dtype=torch.float16, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        lad = d["ladder"]
+        fn = lambda: dmm.rb_encode(W, lad, codes, alpha, row_scale=rs, status=st)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        nbytes = 4 * N * K + N * K + 2 * N + 4          # W once, codes, rho, alpha
+        gbs = nbytes / sec / 1e9
+        res["routeb_encode_per_row"] = {
+            "us_per_call": round(sec * 1e6, 2),
+            "bytes_per_call": int(nbytes),
+            "GBs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "weights_per_s": round(N * K / sec, 1),
+        }
+        del W, codes
 
     if "prefill" in sel:
         progress("extra: routeb_prefill")

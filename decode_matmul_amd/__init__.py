@@ -26,11 +26,12 @@ TQ_DATA_RANGE = 1
 TQ_DATA_CODE = 2
 TQ_DATA_PADDING = 4
 
-EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_matmul", "tq_status_string")
+EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul",
+           "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m decode_matmul_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python decode_matmul_amd/build.py` "
         "(there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -44,10 +45,11 @@ _lib.tq_unpack.argtypes = [_p, _p, _i64, _i64, _i32, _p, _i32, _p, _p]
 _lib.tq_matmul.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i64, _i32, _i32, _p, _i32, _p,
                            _i32, _p]
 _lib.rb_table.argtypes = [_p, _p]
+_lib.rb_encode.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, _i32, _p, _p, _p, _p, _p]
 _lib.rb_matmul.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _p, _p, _i32, _p]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
-for _name in ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_matmul"):
+for _name in ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul"):
     getattr(_lib, _name).restype = _i32
 
 
@@ -178,6 +180,28 @@ def rb_table(ladder):
     rc = _lib.rb_table(a.ctypes.data_as(_p), out.ctypes.data_as(_p))
     _raise(rc, "rb_table")
     return out
+
+
+def rb_encode(W, ladder, codes, alpha_out, zeta=0.0, row_scale=None, status=None):
+    """Route B encoder: fp32 W [N, K] -> codes uint8 [N, K], alpha_out fp32 [1]
+    and, when row_scale (fp16 [N]) is given, the per-row scales."""
+    import numpy as np
+    dev = W.device
+    N, K = W.shape
+    _need(W, "W", _F32, N * K, dev)
+    _need(codes, "codes", _U8, N * K, dev)
+    _need(alpha_out, "alpha_out", _F32, 1, dev)
+    if row_scale is not None:
+        _need(row_scale, "row_scale", _H16, N, dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(status, "status", _I32, 1, dev)
+    a = np.ascontiguousarray(np.asarray(ladder, dtype=np.float32).reshape(5))
+    rc = _lib.rb_encode(_ptr(W), N, K, a.ctypes.data_as(_p), float(zeta),
+                        1 if row_scale is not None else 0, _ptr(codes), _ptr(alpha_out),
+                        _ptr(row_scale), _ptr(status), _stream(dev))
+    _raise(rc, "rb_encode")
+    return status
 
 
 def rb_matmul(x, codes, table, alpha, y, row_scale=None, bias=None):

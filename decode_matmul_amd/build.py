@@ -1,6 +1,6 @@
 """Compile the HIP sources under csrc/ into libdecode_matmul.so (gfx950).
 
-    python -m decode_matmul_amd.build
+    python decode_matmul_amd/build.py
 
 Every call recompiles.  Objects go to decode_matmul_amd/_build/ (ignored by
 git); the shared library lands next to this file, where the binding loads it.

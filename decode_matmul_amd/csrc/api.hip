@@ -51,6 +51,25 @@ int tq_pack(const float* W, int64_t rows, int64_t K, int32_t G, int32_t planes,
                                        d_status, s));
 }
 
+int rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
+              int32_t per_row, uint8_t* codes, float* alpha_out, uint16_t* row_scale,
+              int32_t* d_status, void* stream) {
+    if (!ladder || !alpha_out || !d_status) return TQ_ERR_NULL;
+    if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return TQ_ERR_SHAPE;
+    if (per_row != 0 && per_row != 1) return TQ_ERR_UNSUPPORTED;
+    if (!(zeta >= 0.f && zeta <= 1.f)) return TQ_ERR_UNSUPPORTED;
+    for (int i = 0; i < 5; ++i)                       // finite, nonnegative steps
+        if (!(ladder[i] >= 0.f && ladder[i] <= 3.402823466e38f)) return TQ_ERR_UNSUPPORTED;
+    if (N > 0 && K > 0 && (!W || !codes)) return TQ_ERR_NULL;
+    if (per_row && N > 0 && !row_scale) return TQ_ERR_NULL;
+    if (!per_row && row_scale) return TQ_ERR_SHAPE;
+    if ((W && !aligned(W, 4)) || !aligned(alpha_out, 4) || (row_scale && !aligned(row_scale, 2)) ||
+        !aligned(d_status, 4))
+        return TQ_ERR_ALIGN;
+    return hip_status(dmm::launch_rb_encode(W, N, K, ladder, zeta, per_row, codes, alpha_out,
+                                            row_scale, d_status, (hipStream_t)stream));
+}
+
 int tq_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t K,
               int32_t G, void* W_out, int32_t out_dtype, int32_t* d_status, void* stream) {
     if (!codes || !scales || !W_out || !d_status) return TQ_ERR_NULL;

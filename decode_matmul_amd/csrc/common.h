@@ -128,5 +128,8 @@ struct RbMatmulArgs {
 
 hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s);
 hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s);
+hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
+                            int per_row, uint8_t* codes, float* alpha, uint16_t* row_scale,
+                            int32_t* status, hipStream_t s);
 
 }  // namespace dmm

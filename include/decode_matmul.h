@@ -157,6 +157,39 @@ int tq_matmul(const uint16_t* x, int64_t M, int64_t K,
 int rb_table(const float* ladder, float* table_out);
 
 /*
+ * rb_encode -- the Route B encoder on the device (Route B paper, section 3.1:
+ * the greedy 5-step ternary word of r_0 = x / alpha, each step taking the c
+ * in {-1, 0, +1} nearest to the residual, with a zero-bias zeta that keeps
+ * c_i = 0 while |r_{i-1}| < zeta * s_i; section 3.2: codes are the base-3
+ * encoding of c_1..c_5; section 3.3: the per-row scale).
+ *
+ *  W          device fp32 [N, K] row-major, 4-byte aligned.
+ *  ladder     host fp32 [5], s_1..s_5 (finite, >= 0; the pages' ladders are
+ *             positive).
+ *  zeta       zero-bias in [0, 1] (0: the plain greedy word).
+ *  per_row    0: r_0 = W / alpha with alpha = max |W| over the matrix;
+ *             1: r_0 = W[n, k] / alpha_n with alpha_n = max_k |W[n, k]|.
+ *  codes      device uint8 [N, K]: sum_i (c_i + 1) 3^(5-i) (c_1 most
+ *             significant, the order rb_table enumerates).
+ *  alpha_out  device fp32 [1]: alpha = max |W| (0 for an empty or all-zero W).
+ *  row_scale  device fp16 [N] when per_row (rho_n = fp16(alpha_n / alpha),
+ *             0 when alpha = 0), else NULL.
+ *  d_status   device int32; set to 0, then TQ_DATA_RANGE if a weight is not
+ *             finite (the outputs are then unspecified, memory stays in bounds).
+ *
+ * Decisions are taken on IEEE float64 values: r_0 is one float64 division of
+ * the fp32 weight by the fp32 scale, each residual one float64 subtraction,
+ * ties of the argmin go to c = 0, and rho_n is the float64 quotient rounded
+ * once to fp16.  A zero scale gives the all-zero word (code 121).  Then
+ * rb_matmul(x, codes, rb_table(ladder), alpha, row_scale) applies
+ * W_hat = rho_n * alpha * sum_i c_i s_i.  One call reads W twice (three
+ * times with per_row) and allocates nothing.
+ */
+int rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
+              int32_t per_row, uint8_t* codes, float* alpha_out, uint16_t* row_scale,
+              int32_t* d_status, void* stream);
+
+/*
  * rb_matmul -- Route B matmul (Route B paper, section 4.2: code bytes are
  * dereferenced through the code book inside the GEMM; the per-row scale is
  * applied to the output accumulator before the bias add):
@@ -173,8 +206,10 @@ int rb_table(const float* ladder, float* table_out);
  *
  * M <= 16 runs a GEMV kernel that keeps each weight as an exact split of the
  * table value into two bf16 terms (error < 2^-16 per term); M > 16 runs an
- * MFMA kernel that decodes tiles of bf16 table values into LDS (error <=
- * 2^-9 per term).  Both accumulate in fp32.  Codes 243..255 read a zero
+ * MFMA kernel that multiplies in fp16 against the code book scaled by a power
+ * of two (error <= 2^-11 per term), with activations converted to fp16
+ * exactly and any 8-value chunk fp16 cannot hold replayed on bf16 MFMAs
+ * against the two-term bf16 split.  Both accumulate in fp32.  Codes 243..255 read a zero
  * table entry.  M = 0 or N = 0 is a no-op; with K = 0, x and codes may be
  * NULL and y = bias (or 0).
  */

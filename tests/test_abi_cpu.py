@@ -124,6 +124,39 @@ def test_rb_matmul_argument_errors():
     assert f(*bad) == 0
 
 
+def test_rb_encode_argument_errors():
+    f = lib.rb_encode
+    lad = np.array([1, 1 / 3, 1 / 9, 1 / 27, 1 / 81], np.float32)
+    lp = lad.ctypes.data_as(ctypes.c_void_p)
+    bad_lad = lad.copy()
+    bad_lad[2] = np.nan
+    bp = bad_lad.ctypes.data_as(ctypes.c_void_p)
+    z = ctypes.c_float
+    ok = [FAKE, 4, 64, lp, z(0.0), 0, FAKE, FAKE, None, FAKE, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+
+    assert call(3, None) == TQ_ERR_NULL                # ladder
+    assert call(7, None) == TQ_ERR_NULL                # alpha_out
+    assert call(9, None) == TQ_ERR_NULL                # d_status
+    assert call(0, None) == TQ_ERR_NULL                # W with N, K > 0
+    assert call(6, None) == TQ_ERR_NULL                # codes
+    assert call(1, -1) == TQ_ERR_SHAPE
+    assert call(2, -5) == TQ_ERR_SHAPE
+    assert call(5, 2) == TQ_ERR_UNSUPPORTED            # per_row
+    assert call(4, z(1.5)) == TQ_ERR_UNSUPPORTED       # zeta outside [0, 1]
+    assert call(4, z(-0.1)) == TQ_ERR_UNSUPPORTED
+    assert call(4, z(float("nan"))) == TQ_ERR_UNSUPPORTED
+    assert call(3, bp) == TQ_ERR_UNSUPPORTED           # non-finite ladder step
+    assert call(5, 1) == TQ_ERR_NULL                   # per-row scales without row_scale
+    assert call(8, FAKE) == TQ_ERR_SHAPE               # row_scale without per_row
+    assert call(0, FAKE_ODD) == TQ_ERR_ALIGN
+    assert call(7, FAKE_ODD) == TQ_ERR_ALIGN
+
+
 def test_binding_refuses_wrong_tensors():
     import torch
     x = torch.zeros(1, 64, dtype=torch.float32)

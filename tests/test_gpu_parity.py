@@ -594,3 +594,117 @@ def test_bit_determinism(dmm):
         outs.append([host(t).view(np.uint32) for t in (y1, y2, y3)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ rb_encode
+
+S0_LADDER = np.array([1, 1 / 3, 1 / 9, 1 / 27, 1 / 81], np.float32)
+S_LADDER = np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32)
+
+
+def encode_case(dmm, W, ladder, zeta=0.0, per_row=False):
+    """rb_encode on the device, bit for bit against the oracle's encoder."""
+    N, K = W.shape
+    say(f"rb_encode N={N} K={K} zeta={zeta} per_row={per_row}")
+    codes = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+    alpha = torch.empty(1, dtype=torch.float32, device=DEV)
+    rs = torch.empty(N, dtype=torch.float16, device=DEV) if per_row else None
+    st = dmm.rb_encode(dev(W), ladder, codes, alpha, zeta=zeta, row_scale=rs)
+    assert int(host(st)[0]) == 0
+    c_ref, a_ref, r_ref = oracle.rb_encode(W, ladder, zeta=zeta, per_row=per_row)
+    got = host(codes)
+    assert np.array_equal(got, c_ref), f"{int(np.count_nonzero(got != c_ref))} codes differ"
+    assert host(alpha).view(np.uint32)[0] == np.float32(a_ref).view(np.uint32)
+    if per_row:
+        assert np.array_equal(host(rs.view(torch.int16)).view(np.uint16), r_ref)
+    return codes, alpha, rs
+
+
+def encode_inputs(N, K, seed):
+    """Gaussian weights with per-row magnitudes spread over two decades, plus
+    exact ladder points and half-way points of the first step (ties)."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02 * rng.uniform(0.1, 10.0, (N, 1))).astype(np.float32)
+    if N * K >= 8:
+        a = float(np.abs(W).max())
+        flat = W.reshape(-1)
+        idx = rng.choice(flat.size, min(flat.size // 4, 64), replace=False)
+        flat[idx[0::2]] = np.float32(a / 2) * rng.choice([-1, 1], idx[0::2].size)
+        flat[idx[1::2]] = np.float32(a / 3) * rng.choice([-1, 1], idx[1::2].size)
+    return W
+
+
+ENCODE_SHAPES = [(1, 1), (3, 70), (17, 1000), (64, 4096), (300, 257)]
+
+
+@pytest.mark.parametrize("N,K", ENCODE_SHAPES)
+def test_rb_encode_shapes(dmm, N, K):
+    W = encode_inputs(N, K, seed=N + K)
+    for lad in (S0_LADDER, S_LADDER):
+        for per_row in (False, True):
+            encode_case(dmm, W, lad, zeta=0.0, per_row=per_row)
+    encode_case(dmm, W, S_LADDER, zeta=0.8, per_row=True)
+    encode_case(dmm, W, S0_LADDER, zeta=1.0, per_row=False)
+
+
+def test_rb_encode_worked_examples_and_ties(dmm):
+    """The hand-worked words (tie at |r| = s_1 / 2 goes to 0), and a matrix
+    made only of ladder points and midpoints."""
+    W = np.array([[0.9, -0.5, 1.0, 0.0]], np.float32)
+    for zeta in (0.0, 1.0):
+        codes, _, _ = encode_case(dmm, W, S0_LADDER, zeta=zeta)
+        want = [194, 81, 202, 121] if zeta == 0 else [161, 81, 202, 121]
+        assert list(host(codes)[0]) == want
+    pts = np.array([0.5, -0.5, 1 / 6, -1 / 6, 1 / 3, 2 / 3, 1.0, -1.0, 1 / 162, 0.0], np.float32)
+    encode_case(dmm, np.tile(pts, (5, 3)), S0_LADDER)
+
+
+def test_rb_encode_zero_rows_empty_and_bad_values(dmm):
+    W = np.zeros((6, 40), np.float32)
+    W[2] = np.linspace(-1, 1, 40, dtype=np.float32)
+    encode_case(dmm, W, S_LADDER, per_row=True)
+    encode_case(dmm, np.zeros((3, 5), np.float32), S_LADDER, per_row=True)
+    # K = 0: alpha = 0, rho = 0 for every row; N = 0: only alpha
+    alpha = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
+    rs = torch.full((4,), 1.0, dtype=torch.float16, device=DEV)
+    say("rb_encode K=0")
+    dmm.rb_encode(torch.empty((4, 0), dtype=torch.float32, device=DEV), S_LADDER,
+                  torch.empty((4, 0), dtype=torch.uint8, device=DEV), alpha, row_scale=rs)
+    assert float(host(alpha)[0]) == 0.0 and np.all(host(rs.view(torch.int16)) == 0)
+    say("rb_encode N=0")
+    alpha.fill_(7.0)
+    dmm.rb_encode(torch.empty((0, 8), dtype=torch.float32, device=DEV), S_LADDER,
+                  torch.empty((0, 8), dtype=torch.uint8, device=DEV), alpha)
+    assert float(host(alpha)[0]) == 0.0
+    for bad in (np.nan, np.inf):
+        W2 = encode_inputs(5, 33, seed=9)
+        W2[3, 7] = bad
+        codes = torch.empty((5, 33), dtype=torch.uint8, device=DEV)
+        say(f"rb_encode non-finite {bad}")
+        st = dmm.rb_encode(dev(W2), S_LADDER, codes, alpha)
+        assert int(host(st)[0]) & 1
+
+
+def test_rb_encode_then_matmul(dmm):
+    """Section 3.3 end to end: encode W on the device, then rb_matmul with
+    the device's codes, alpha and rho against the oracle's W_hat."""
+    N, K, M = 200, 768, 5
+    W = encode_inputs(N, K, seed=31)
+    rng = np.random.default_rng(32)
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    codes, alpha, rs = encode_case(dmm, W, S_LADDER, per_row=True)
+    table = oracle.rb_table(S_LADDER)
+    a = float(host(alpha)[0])
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    dmm.rb_matmul(dev(bits16(xb)), codes, dev(table), np.float32(a), y, rs)
+    c_ref, a_ref, r_ref = oracle.rb_encode(W, S_LADDER, per_row=True)
+    w = oracle.rb_weights(c_ref, table, a_ref, r_ref)
+    y_ref, B = oracle.matmul_ref(xb, w)
+    assert_bound(y_host(y), y_ref, B, "encode then matmul")
+
+
+def test_rb_encode_large(dmm):
+    """4096 x 4096 Gaussian weights, per-row and global scales."""
+    W = encode_inputs(4096, 4096, seed=41)
+    encode_case(dmm, W, S_LADDER, per_row=True)
+    encode_case(dmm, W, S0_LADDER, per_row=False)

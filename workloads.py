@@ -80,6 +80,15 @@ def moe_two_plane(seed=3, E=64, N=2048, K=4096, T=16, top_k=8):
     return {"W": W, "x": x, "ids": ids.astype(np.int32), "G": 64}
 
 
+def routeb_encode(seed=5, N=8192, K=8192):
+    """fp32 weights for the Route B encoder: Gaussian rows whose scales
+    spread over two decades (so per-row scales matter), and a ladder."""
+    rng = np.random.default_rng(seed)
+    row_mag = rng.uniform(0.1, 10.0, size=(N, 1))
+    W = (rng.standard_normal((N, K)) * 0.02 * row_mag).astype(np.float32)
+    return {"W": W, "ladder": _ladder(rng)}
+
+
 def routeb_prefill(seed=4, N=8192, K=8192, M=2048):
     rng = np.random.default_rng(seed)
     codes = rng.integers(0, 243, size=(N, K), dtype=np.uint8)
