@@ -44,7 +44,7 @@ from .ternary import (
     quantize_pack,
     two_plane,
 )
-from .routeb import code_words, rb_encode, rb_table, rb_weights
+from .routeb import code_words, rb_block_scales, rb_encode, rb_table, rb_weights
 from .matmul import (
     REL_BOUND,
     matmul_ref,
@@ -57,6 +57,6 @@ __all__ = [
     "f64_to_f16_bits", "f16_bits_to_f64", "f64_to_bf16_bits", "bf16_bits_to_f64", "f64_to_f32",
     "OracleDataError", "bytes_per_group", "bits_per_weight", "quantize", "pack",
     "unpack", "quantize_pack", "two_plane",
-    "code_words", "rb_encode", "rb_table", "rb_weights",
+    "code_words", "rb_block_scales", "rb_encode", "rb_table", "rb_weights",
     "REL_BOUND", "matmul_ref", "ternary_weights", "grouped_ref", "check_bound",
 ]

@@ -45,6 +45,13 @@ rho_n = alpha_n / alpha stored in fp16).  Readings where the page is silent:
 * rho_n is the float64 quotient alpha_n / alpha rounded once to fp16
   (nearest-even); alpha itself is returned as the fp32 value max |W|.
 * Non-finite weights are an error (the scale would not be defined).
+
+Per-head prosody (section 8.2: one rho per attention head, the rows of a
+head sharing a scale) is the same rule over blocks of consecutive rows:
+with rho_rows = b, block h = rows [h b, (h + 1) b) is normalised by its
+largest |W| (alpha_h) and rho_h = fp16(alpha_h / alpha); rho_rows = 1 is the
+per-row scale of section 3.3, and the decoded weight of row n uses
+rho_{n // b}.
 """
 
 import numpy as np
@@ -71,21 +78,40 @@ def rb_table(ladder):
     return f64_to_f32(acc)
 
 
-def rb_weights(codes, table, alpha, row_scale_bits=None):
-    """codes uint8 [N, K] -> W_hat float64 [N, K] = alpha * T[code] * rho_n."""
+def rb_weights(codes, table, alpha, row_scale_bits=None, rho_rows=1):
+    """codes uint8 [N, K] -> W_hat float64 [N, K] = alpha * T[code] * rho,
+    rho of row n being row_scale[n // rho_rows]."""
     codes = np.asarray(codes, dtype=np.uint8)
     t256 = np.zeros(256, dtype=np.float64)
     t256[:243] = np.asarray(table, dtype=np.float32).astype(np.float64)
     w = float(np.float32(alpha)) * t256[codes]
     if row_scale_bits is not None:
         rho = f16_bits_to_f64(row_scale_bits)
-        w = w * rho[:, None]
+        w = w * rho[np.arange(codes.shape[0]) // rho_rows][:, None]
     return w
 
 
-def rb_encode(W, ladder, zeta=0.0, per_row=False):
+def rb_block_scales(W, rho_rows):
+    """alpha_h float32 [ceil(N / rho_rows)]: the largest |W| of each block of
+    rho_rows consecutive rows (0 for an empty block)."""
+    a = np.abs(np.asarray(W, dtype=np.float32))
+    N = a.shape[0]
+    nb = -(-N // rho_rows)
+    out = np.zeros(nb, dtype=np.float32)
+    for h in range(nb):
+        blk = a[h * rho_rows:(h + 1) * rho_rows]
+        out[h] = blk.max() if blk.size else 0.0
+    return out
+
+
+def rb_encode(W, ladder, zeta=0.0, per_row=False, rho_rows=None):
     """Route B encoder: W float32 [N, K] -> (codes uint8 [N, K], alpha float32,
-    rho fp16 bits uint16 [N] or None).  Section 3.1 steps, section 3.3 scales."""
+    rho fp16 bits uint16 [ceil(N / rho_rows)] or None).  Section 3.1 steps,
+    section 3.3 scales (per_row, i.e. rho_rows = 1) or section 8.2 per-head
+    blocks (rho_rows = head rows); rho_rows = 0 (the default without per_row)
+    is the global scale alone."""
+    if rho_rows is None:
+        rho_rows = 1 if per_row else 0
     W = np.asarray(W, dtype=np.float32)
     if W.ndim != 2:
         raise ValueError("W is a matrix")
@@ -97,8 +123,9 @@ def rb_encode(W, ladder, zeta=0.0, per_row=False):
     a = np.abs(W.astype(np.float64))
     alpha = float(a.max()) if W.size else 0.0            # max |W|: an fp32 value
     N, K = W.shape
-    if per_row:
-        scale = a.max(axis=1) if K else np.zeros(N)        # alpha_n
+    if rho_rows > 0:
+        blocks = rb_block_scales(W, rho_rows).astype(np.float64)   # alpha_h
+        scale = blocks[np.arange(N) // rho_rows]
     else:
         scale = np.full(N, alpha)
     r = np.zeros((N, K), dtype=np.float64)
@@ -117,9 +144,9 @@ def rb_encode(W, ladder, zeta=0.0, per_row=False):
         r = r - c * s[i]
         codes = codes * 3 + (c + 1)                        # c_1 most significant
     rho = None
-    if per_row:
-        q = np.zeros(N, dtype=np.float64)
+    if rho_rows > 0:
+        q = np.zeros(blocks.size, dtype=np.float64)
         if alpha > 0:
-            q = scale / alpha
+            q = blocks / alpha
         rho = f64_to_f16_bits(q)
     return codes.astype(np.uint8), np.float32(alpha), rho

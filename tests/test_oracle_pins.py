@@ -695,3 +695,36 @@ def test_encode_zero_bias_below_one_half_changes_nothing():
     c1, _, _ = oracle.rb_encode(W, lad, zeta=1.0)
     w0, w1 = oracle.code_words()[c0], oracle.code_words()[c1]
     assert np.count_nonzero(w1) < np.count_nonzero(w0)
+
+
+def test_encode_head_blocks():
+    """Section 8.2 per-head prosody as row blocks: one block equals the
+    global encoding with rho = 1; blocks of one row equal the per-row scale;
+    each block's largest |W| spells (+-1, 0, 0, 0, 0) under S0; rho_h is
+    numpy's fp16 of alpha_h / alpha; a ragged last block works; and the
+    decoded weight of row n uses rho_{n // b}."""
+    lad = _ladders()["S0"]
+    rng = np.random.default_rng(7)
+    N, K, b = 10, 40, 4
+    W = (rng.standard_normal((N, K)) * rng.uniform(0.05, 2.0, (N, 1))).astype(np.float32)
+    cg, ag, _ = oracle.rb_encode(W, lad)
+    c1, a1, r1 = oracle.rb_encode(W, lad, rho_rows=N)
+    assert np.array_equal(c1, cg) and a1 == ag and list(r1) == [np.float16(1).view(np.uint16)]
+    cr, _, rr = oracle.rb_encode(W, lad, per_row=True)
+    cb, _, rb = oracle.rb_encode(W, lad, rho_rows=1)
+    assert np.array_equal(cr, cb) and np.array_equal(rr, rb)
+    codes, alpha, rho = oracle.rb_encode(W, lad, rho_rows=b)
+    assert rho.shape == (3,)                           # rows 8, 9 form the last block
+    a_h = oracle.rb_block_scales(W, b)
+    for h in range(3):
+        blk = np.abs(W[h * b:(h + 1) * b])
+        assert a_h[h] == blk.max()
+        n, k = np.unravel_index(int(np.argmax(blk)), blk.shape)
+        n += h * b
+        assert int(codes[n, k]) == (202 if W[n, k] > 0 else 40)
+    want = (a_h.astype(np.float64) / float(alpha)).astype(np.float16).view(np.uint16)
+    assert np.array_equal(rho, want)
+    T = oracle.rb_table(lad)
+    per_row_rho = np.repeat(rho, b)[:N]
+    assert np.array_equal(oracle.rb_weights(codes, T, alpha, rho, rho_rows=b),
+                          oracle.rb_weights(codes, T, alpha, per_row_rho))
