@@ -379,13 +379,13 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         N, K = d["W"].shape
         W = to_dev(d["W"])
         codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
-        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+        alpha = torch.empty(1 + N, dtype=torch.float32, device=dev)
         rs = torch.empty(N, dtype=torch.float16, device=dev)
         st = torch.zeros(1, dtype=torch.int32, device=dev)
         lad = d["ladder"]
         fn = lambda: dmm.rb_encode(W, lad, codes, alpha, row_scale=rs, status=st)
         sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
-        nbytes = 4 * N * K + N * K + 2 * N + 4          # W once, codes, rho, alpha
+        nbytes = 4 * N * K + N * K + 6 * N + 4          # W once, codes, rho, alpha_n, alpha
         gbs = nbytes / sec / 1e9
         res["routeb_encode_per_row"] = {
             "us_per_call": round(sec * 1e6, 2),

@@ -27,7 +27,7 @@ TQ_DATA_CODE = 2
 TQ_DATA_PADDING = 4
 
 EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul",
-           "tq_status_string")
+           "rb_matmul_rho_block", "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -47,9 +47,12 @@ _lib.tq_matmul.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i64, _i32, _i32, _p,
 _lib.rb_table.argtypes = [_p, _p]
 _lib.rb_encode.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, _i32, _p, _p, _p, _p, _p]
 _lib.rb_matmul.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _p, _p, _i32, _p]
+_lib.rb_matmul_rho_block.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _i32, _p,
+                                     _p, _i32, _p]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
-for _name in ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul"):
+for _name in ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul",
+              "rb_matmul_rho_block"):
     getattr(_lib, _name).restype = _i32
 
 
@@ -182,30 +185,35 @@ def rb_table(ladder):
     return out
 
 
-def rb_encode(W, ladder, codes, alpha_out, zeta=0.0, row_scale=None, status=None):
-    """Route B encoder: fp32 W [N, K] -> codes uint8 [N, K], alpha_out fp32 [1]
-    and, when row_scale (fp16 [N]) is given, the per-row scales."""
+def rb_encode(W, ladder, codes, alpha_out, zeta=0.0, row_scale=None, rho_rows=None,
+              status=None):
+    """Route B encoder: fp32 W [N, K] -> codes uint8 [N, K] and alpha_out fp32.
+    Without row_scale: one global scale, alpha_out [1].  With row_scale (fp16
+    [ceil(N / rho_rows)], rho_rows 1 by default): one scale per block of
+    rho_rows rows, alpha_out [1 + ceil(N / rho_rows)]."""
     import numpy as np
     dev = W.device
     N, K = W.shape
+    b = 0 if row_scale is None else (1 if rho_rows is None else int(rho_rows))
+    nb = -(-N // b) if b > 0 else 0
     _need(W, "W", _F32, N * K, dev)
     _need(codes, "codes", _U8, N * K, dev)
-    _need(alpha_out, "alpha_out", _F32, 1, dev)
+    _need(alpha_out, "alpha_out", _F32, 1 + nb, dev)
     if row_scale is not None:
-        _need(row_scale, "row_scale", _H16, N, dev)
+        _need(row_scale, "row_scale", _H16, nb, dev)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     _need(status, "status", _I32, 1, dev)
     a = np.ascontiguousarray(np.asarray(ladder, dtype=np.float32).reshape(5))
-    rc = _lib.rb_encode(_ptr(W), N, K, a.ctypes.data_as(_p), float(zeta),
-                        1 if row_scale is not None else 0, _ptr(codes), _ptr(alpha_out),
-                        _ptr(row_scale), _ptr(status), _stream(dev))
+    rc = _lib.rb_encode(_ptr(W), N, K, a.ctypes.data_as(_p), float(zeta), b, _ptr(codes),
+                        _ptr(alpha_out), _ptr(row_scale), _ptr(status), _stream(dev))
     _raise(rc, "rb_encode")
     return status
 
 
-def rb_matmul(x, codes, table, alpha, y, row_scale=None, bias=None):
-    """y = alpha * rho * (x T[codes]^T) + bias for uint8 codes [N, K]."""
+def rb_matmul(x, codes, table, alpha, y, row_scale=None, bias=None, rho_rows=1):
+    """y = alpha * rho * (x T[codes]^T) + bias for uint8 codes [N, K]; rho of
+    row n is row_scale[n // rho_rows]."""
     dev = x.device
     M, K = x.shape
     N = codes.shape[0]
@@ -213,12 +221,17 @@ def rb_matmul(x, codes, table, alpha, y, row_scale=None, bias=None):
     _need(codes, "codes", _U8, N * K, dev)
     _need(table, "table", _F32, 243, dev)
     if row_scale is not None:
-        _need(row_scale, "row_scale", _H16, N, dev)
+        _need(row_scale, "row_scale", _H16, -(-N // int(rho_rows)) if rho_rows > 0 else N, dev)
     if bias is not None:
         _need(bias, "bias", _F32, N, dev)
     _need(y, "y", (y.dtype,), M * N, dev)
-    rc = _lib.rb_matmul(_ptr(x), M, K, _ptr(codes), N, _ptr(table), float(alpha),
-                        _ptr(row_scale), _ptr(bias), _ptr(y), _ydtype(y), _stream(dev))
+    if rho_rows == 1:
+        rc = _lib.rb_matmul(_ptr(x), M, K, _ptr(codes), N, _ptr(table), float(alpha),
+                            _ptr(row_scale), _ptr(bias), _ptr(y), _ydtype(y), _stream(dev))
+    else:
+        rc = _lib.rb_matmul_rho_block(_ptr(x), M, K, _ptr(codes), N, _ptr(table), float(alpha),
+                                      _ptr(row_scale), int(rho_rows), _ptr(bias), _ptr(y),
+                                      _ydtype(y), _stream(dev))
     _raise(rc, "rb_matmul")
 
 

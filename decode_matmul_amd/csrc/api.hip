@@ -52,21 +52,21 @@ int tq_pack(const float* W, int64_t rows, int64_t K, int32_t G, int32_t planes,
 }
 
 int rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
-              int32_t per_row, uint8_t* codes, float* alpha_out, uint16_t* row_scale,
+              int32_t rho_rows, uint8_t* codes, float* alpha_out, uint16_t* row_scale,
               int32_t* d_status, void* stream) {
     if (!ladder || !alpha_out || !d_status) return TQ_ERR_NULL;
     if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return TQ_ERR_SHAPE;
-    if (per_row != 0 && per_row != 1) return TQ_ERR_UNSUPPORTED;
+    if (rho_rows < 0) return TQ_ERR_SHAPE;
     if (!(zeta >= 0.f && zeta <= 1.f)) return TQ_ERR_UNSUPPORTED;
     for (int i = 0; i < 5; ++i)                       // finite, nonnegative steps
         if (!(ladder[i] >= 0.f && ladder[i] <= 3.402823466e38f)) return TQ_ERR_UNSUPPORTED;
     if (N > 0 && K > 0 && (!W || !codes)) return TQ_ERR_NULL;
-    if (per_row && N > 0 && !row_scale) return TQ_ERR_NULL;
-    if (!per_row && row_scale) return TQ_ERR_SHAPE;
+    if (rho_rows > 0 && N > 0 && !row_scale) return TQ_ERR_NULL;
+    if (rho_rows == 0 && row_scale) return TQ_ERR_SHAPE;
     if ((W && !aligned(W, 4)) || !aligned(alpha_out, 4) || (row_scale && !aligned(row_scale, 2)) ||
         !aligned(d_status, 4))
         return TQ_ERR_ALIGN;
-    return hip_status(dmm::launch_rb_encode(W, N, K, ladder, zeta, per_row, codes, alpha_out,
+    return hip_status(dmm::launch_rb_encode(W, N, K, ladder, zeta, rho_rows, codes, alpha_out,
                                             row_scale, d_status, (hipStream_t)stream));
 }
 
@@ -147,8 +147,17 @@ int rb_table(const float* ladder, float* table_out) {
 int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
               const float* table, float alpha, const uint16_t* row_scale, const float* bias,
               void* y, int32_t y_dtype, void* stream) {
+    return rb_matmul_rho_block(x, M, K, codes, N, table, alpha, row_scale, 1, bias, y, y_dtype,
+                               stream);
+}
+
+int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                        const float* table, float alpha, const uint16_t* row_scale,
+                        int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
+                        void* stream) {
     if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
         return TQ_ERR_SHAPE;
+    if (rho_rows < 1) return TQ_ERR_SHAPE;
     if (y_dtype != TQ_F32 && y_dtype != TQ_BF16) return TQ_ERR_DTYPE;
     if (M == 0 || N == 0) return TQ_OK;
     if (!table || !y || (K > 0 && (!x || !codes))) return TQ_ERR_NULL;
@@ -164,6 +173,7 @@ int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int
     a.table = table;
     a.alpha = alpha;
     a.row_scale = row_scale;
+    a.rho_rows = rho_rows;
     a.bias = bias;
     a.y = y;
     a.y_dtype = y_dtype;

@@ -121,6 +121,7 @@ struct RbMatmulArgs {
     const float* table;
     float alpha;
     const uint16_t* row_scale;
+    int64_t rho_rows;       // rows sharing one row_scale entry (>= 1)
     const float* bias;
     void* y;
     int y_dtype;
@@ -129,7 +130,7 @@ struct RbMatmulArgs {
 hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s);
 hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s);
 hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
-                            int per_row, uint8_t* codes, float* alpha, uint16_t* row_scale,
+                            int64_t rho_rows, uint8_t* codes, float* alpha, uint16_t* row_scale,
                             int32_t* status, hipStream_t s);
 
 }  // namespace dmm

@@ -1,5 +1,5 @@
 // Route B encoder: fp32 W -> code bytes, the global scale alpha and the
-// optional fp16 per-row scales.
+// optional fp16 row or head scales.
 //
 // Semantics: "A Discrete Weight Language for Large Language Models" (Route
 // B), section 3.1 (the greedy 5-step word: each step takes the c in
@@ -7,22 +7,25 @@
 // with alpha = max |W|; a zero-bias zeta forces c_i = 0 while
 // |r_{i-1}| < zeta s_i), section 3.2 (the code is the base-3 encoding of
 // c_1..c_5) and section 3.3 (per-row scale: r_0 = W[n, k] / alpha_n with
-// alpha_n = max_k |W[n, k]|, rho_n = alpha_n / alpha in fp16).
+// alpha_n = max_k |W[n, k]|, rho_n = alpha_n / alpha in fp16).  Per-head
+// prosody (section 8.2: one rho per attention head, the rows of a head
+// sharing the scale) is the same rule over blocks of rho_rows consecutive
+// rows: alpha_h is the block's largest |W| and rho_h = fp16(alpha_h / alpha);
+// rho_rows = 1 is section 3.3, rho_rows = 0 the global scale alone.
 //
 // Every decision is taken on IEEE float64 values: r_0 is one float64
 // division, each residual one float64 subtraction (c s_i is exact), the
 // distances |r - s_i|, |r|, |r + s_i| and zeta s_i are float64, ties go to
-// c = 0, and rho_n is one float64 division rounded once to fp16 (on the bit
+// c = 0, and rho_h is one float64 division rounded once to fp16 (on the bit
 // pattern).  So the codes do not depend on the order of operations or on the
 // hardware.  A zero scale gives r_0 = 0 (the all-zero word, code 121) and
-// rho_n = 0.
+// rho_h = 0.
 //
-// Two launches after the clear: a grid-stride max |W| (atomic max on the
-// bits of the non-negative float, which order like integers; non-finite
-// weights raise TQ_DATA_RANGE), then one workgroup per row that finds the
-// row maximum when per-row scales are asked for and encodes the row.  Not on
-// the timed path of a matmul; it reads W twice (three times with per-row
-// scales) and writes one byte per weight.
+// Three launches: a clear of alpha and the block scales; one workgroup per
+// row taking the row's max |W| into alpha and into its block's scale (atomic
+// max on the bits of the non-negative float, which order like integers;
+// non-finite weights raise TQ_DATA_RANGE); one workgroup per row that
+// encodes it (the block's first row also writes rho_h).  W is read twice.
 #include "common.h"
 
 namespace dmm {
@@ -36,36 +39,51 @@ struct EncParams {
     int64_t N, K;
     double s[5];             // the ladder as float64 (each >= 0)
     double zs[5];            // zeta * s_i, float64 products
-    int per_row;
+    int64_t rho_rows;        // 0: global scale; b: one scale per b rows
     uint8_t* codes;
-    float* alpha;            // device fp32: max |W| (written by the first pass)
-    uint16_t* row_scale;     // device fp16 [N] when per_row
+    float* alpha;            // device fp32 [1 + blocks]: max |W|, then alpha_h
+    uint16_t* row_scale;     // device fp16 [blocks] when rho_rows > 0
     int32_t* status;
 };
 
-__global__ void enc_clear_kernel(float* alpha, int32_t* status) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        *alpha = 0.f;
-        *status = 0;
-    }
+__global__ void enc_clear_kernel(float* alpha, int64_t n, int32_t* status) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        alpha[i] = 0.f;
+    if (threadIdx.x == 0 && blockIdx.x == 0) *status = 0;
 }
 
-// Largest |W| over the matrix.
-__global__ void __launch_bounds__(kEncThreads) enc_absmax_kernel(const float* W, int64_t n,
-                                                                 float* alpha, int32_t* status) {
+__device__ __forceinline__ float block_max(float m, float* red) {
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = m;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kEncThreads / 64; ++w) r = fmaxf(r, red[w]);
+    return r;
+}
+
+// Largest |W| of row blockIdx.x into alpha[0] and (blocks) alpha[1 + n / b].
+__global__ void __launch_bounds__(kEncThreads) enc_rowmax_kernel(EncParams p) {
+    __shared__ float red[kEncThreads / 64];
+    const int64_t n = blockIdx.x;
+    const float* row = p.W + n * p.K;
     float m = 0.f;
     bool finite = true;
-    const int64_t stride = (int64_t)gridDim.x * kEncThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x; i < n; i += stride) {
-        const float a = fabsf(W[i]);
+    for (int64_t k = threadIdx.x; k < p.K; k += kEncThreads) {
+        const float a = fabsf(row[k]);
         finite = finite && (a <= 3.402823466e38f);
         m = fmaxf(m, a);
     }
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    const bool bad = __builtin_amdgcn_ballot_w64(!finite) != 0;
-    if ((threadIdx.x & 63) == 0) {
-        atomicMax((unsigned int*)alpha, __builtin_bit_cast(unsigned int, m));
-        if (bad) atomicOr(status, (int32_t)TQ_DATA_RANGE);
+    const bool bad = __syncthreads_or(!finite) != 0;
+    const float rm = block_max(m, red);
+    if (threadIdx.x == 0) {
+        atomicMax((unsigned int*)p.alpha, __builtin_bit_cast(unsigned int, rm));
+        if (p.rho_rows > 0)
+            atomicMax((unsigned int*)(p.alpha + 1 + n / p.rho_rows),
+                      __builtin_bit_cast(unsigned int, rm));
+        if (bad) atomicOr(p.status, (int32_t)TQ_DATA_RANGE);
     }
 }
 
@@ -89,31 +107,18 @@ __device__ __forceinline__ uint32_t encode_word(double r, const EncParams& p) {
     return code;
 }
 
-__device__ __forceinline__ float block_max(float m, float* red) {
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = m;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < kEncThreads / 64; ++w) r = fmaxf(r, red[w]);
-    return r;
-}
-
 __global__ void __launch_bounds__(kEncThreads) enc_rows_kernel(EncParams p) {
-    __shared__ float red[kEncThreads / 64];
     const int64_t n = blockIdx.x;
     const float* row = p.W + n * p.K;
-    float scale = *p.alpha;
-    if (p.per_row) {
-        float m = 0.f;
-        for (int64_t k = threadIdx.x; k < p.K; k += kEncThreads) m = fmaxf(m, fabsf(row[k]));
-        const float an = block_max(m, red);
-        if (threadIdx.x == 0) {
-            const double q = scale > 0.f ? (double)an / (double)scale : 0.0;
-            p.row_scale[n] = f64_to_f16_rne(q);
+    const float alpha = p.alpha[0];
+    float scale = alpha;
+    if (p.rho_rows > 0) {
+        const int64_t h = n / p.rho_rows;
+        scale = p.alpha[1 + h];
+        if (threadIdx.x == 0 && n == h * p.rho_rows) {
+            const double q = alpha > 0.f ? (double)scale / (double)alpha : 0.0;
+            p.row_scale[h] = f64_to_f16_rne(q);
         }
-        scale = an;
     }
     const double ds = (double)scale;
     const bool pos = scale > 0.f;
@@ -127,21 +132,15 @@ __global__ void __launch_bounds__(kEncThreads) enc_rows_kernel(EncParams p) {
 }  // namespace
 
 hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
-                            int per_row, uint8_t* codes, float* alpha, uint16_t* row_scale,
+                            int64_t rho_rows, uint8_t* codes, float* alpha, uint16_t* row_scale,
                             int32_t* status, hipStream_t s) {
-    hipLaunchKernelGGL(enc_clear_kernel, dim3(1), dim3(64), 0, s, alpha, status);
+    const int64_t blocks = rho_rows > 0 ? (N + rho_rows - 1) / rho_rows : 0;
+    const int64_t nclear = 1 + blocks;
+    const int64_t cg = (nclear + 255) / 256;
+    hipLaunchKernelGGL(enc_clear_kernel, dim3((unsigned)(cg < 1024 ? cg : 1024)), dim3(256), 0, s,
+                       alpha, nclear, status);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t total = N * K;
-    if (total > 0) {
-        const int64_t want = (total + kEncThreads * 16 - 1) / (kEncThreads * 16);
-        const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
-        hipLaunchKernelGGL(enc_absmax_kernel, dim3(blocks), dim3(kEncThreads), 0, s, W, total, alpha,
-                           status);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (N == 0) return hipSuccess;
+    if (e != hipSuccess || N == 0) return e;
     EncParams p;
     p.W = W;
     p.N = N;
@@ -150,11 +149,14 @@ hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* l
         p.s[i] = (double)ladder[i];
         p.zs[i] = (double)zeta * p.s[i];
     }
-    p.per_row = per_row;
+    p.rho_rows = rho_rows;
     p.codes = codes;
     p.alpha = alpha;
     p.row_scale = row_scale;
     p.status = status;
+    hipLaunchKernelGGL(enc_rowmax_kernel, dim3((unsigned)N), dim3(kEncThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(enc_rows_kernel, dim3((unsigned)N), dim3(kEncThreads), 0, s, p);
     return hipGetLastError();
 }

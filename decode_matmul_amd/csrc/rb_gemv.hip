@@ -50,6 +50,7 @@ struct Params {
     const float* table;
     float alpha;
     const uint16_t* row_scale;
+    int64_t rho_rows;                        // rows sharing one row_scale entry
     const float* bias;
     void* y;
     int y_dtype;
@@ -287,7 +288,7 @@ rb_gemv_kernel(Params p) {
     if (wave < kRB) {
         const int r = wave;
         if (row_ok[r]) {
-            const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n[r]]) : 1.f;
+            const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n[r] / p.rho_rows]) : 1.f;
             const float bias = p.bias ? p.bias[n[r]] : 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -418,7 +419,7 @@ rb_gemv_tiled_kernel(Params p) {
     if (wave == 0) {
         const int64_t n = row0 + col;
         if (n < p.N) {
-            const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
+            const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n / p.rho_rows]) : 1.f;
             const float bias = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -449,6 +450,7 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
     p.table = a.table;
     p.alpha = a.alpha;
     p.row_scale = a.row_scale;
+    p.rho_rows = a.rho_rows;
     p.bias = a.bias;
     p.y = a.y;
     p.y_dtype = a.y_dtype;

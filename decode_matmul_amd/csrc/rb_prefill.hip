@@ -67,6 +67,7 @@ struct Params {
     const float* table;
     float alpha;
     const uint16_t* row_scale;
+    int64_t rho_rows;                        // rows sharing one row_scale entry
     const float* bias;
     void* y;
     int y_dtype;
@@ -422,7 +423,7 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     for (int jn = 0; jn < NT; ++jn) {
         const int64_t n = n0 + wn * 32 * NT + jn * 32 + (lane & 31);
         if (n >= p.N) continue;
-        const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n]) : 1.f;
+        const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n / p.rho_rows]) : 1.f;
         const float bias = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -454,6 +455,7 @@ hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s) {
     p.table = a.table;
     p.alpha = a.alpha;
     p.row_scale = a.row_scale;
+    p.rho_rows = a.rho_rows;
     p.bias = a.bias;
     p.y = a.y;
     p.y_dtype = a.y_dtype;

@@ -158,35 +158,40 @@ int rb_table(const float* ladder, float* table_out);
 
 /*
  * rb_encode -- the Route B encoder on the device (Route B paper, section 3.1:
- * the greedy 5-step ternary word of r_0 = x / alpha, each step taking the c
+ * the greedy 5-step ternary word of r_0 = x / scale, each step taking the c
  * in {-1, 0, +1} nearest to the residual, with a zero-bias zeta that keeps
  * c_i = 0 while |r_{i-1}| < zeta * s_i; section 3.2: codes are the base-3
- * encoding of c_1..c_5; section 3.3: the per-row scale).
+ * encoding of c_1..c_5; section 3.3: the per-row scale; section 8.2: one
+ * scale per attention head, i.e. per block of consecutive rows).
  *
  *  W          device fp32 [N, K] row-major, 4-byte aligned.
  *  ladder     host fp32 [5], s_1..s_5 (finite, >= 0; the pages' ladders are
  *             positive).
  *  zeta       zero-bias in [0, 1] (0: the plain greedy word).
- *  per_row    0: r_0 = W / alpha with alpha = max |W| over the matrix;
- *             1: r_0 = W[n, k] / alpha_n with alpha_n = max_k |W[n, k]|.
+ *  rho_rows   0: r_0 = W / alpha with alpha = max |W| over the matrix;
+ *             b >= 1: rows are taken in blocks h of b consecutive rows (the
+ *             last one may be shorter), r_0 = W[n, k] / alpha_h with
+ *             alpha_h the block's largest |W| (b = 1: per row; b = head_dim:
+ *             per attention head).
  *  codes      device uint8 [N, K]: sum_i (c_i + 1) 3^(5-i) (c_1 most
  *             significant, the order rb_table enumerates).
- *  alpha_out  device fp32 [1]: alpha = max |W| (0 for an empty or all-zero W).
- *  row_scale  device fp16 [N] when per_row (rho_n = fp16(alpha_n / alpha),
- *             0 when alpha = 0), else NULL.
+ *  alpha_out  device fp32 [1] when rho_rows = 0, else [1 + ceil(N / b)]:
+ *             alpha = max |W| (0 for an empty or all-zero W), then alpha_h.
+ *  row_scale  device fp16 [ceil(N / b)] when rho_rows > 0 (rho_h =
+ *             fp16(alpha_h / alpha), 0 when alpha = 0), else NULL.
  *  d_status   device int32; set to 0, then TQ_DATA_RANGE if a weight is not
  *             finite (the outputs are then unspecified, memory stays in bounds).
  *
  * Decisions are taken on IEEE float64 values: r_0 is one float64 division of
  * the fp32 weight by the fp32 scale, each residual one float64 subtraction,
- * ties of the argmin go to c = 0, and rho_n is the float64 quotient rounded
+ * ties of the argmin go to c = 0, and rho_h is the float64 quotient rounded
  * once to fp16.  A zero scale gives the all-zero word (code 121).  Then
- * rb_matmul(x, codes, rb_table(ladder), alpha, row_scale) applies
- * W_hat = rho_n * alpha * sum_i c_i s_i.  One call reads W twice (three
- * times with per_row) and allocates nothing.
+ * rb_matmul_rho_block(x, codes, rb_table(ladder), alpha, row_scale, b)
+ * applies W_hat[n, k] = rho_{n / b} * alpha * sum_i c_i s_i.  One call reads
+ * W twice and allocates nothing.
  */
 int rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
-              int32_t per_row, uint8_t* codes, float* alpha_out, uint16_t* row_scale,
+              int32_t rho_rows, uint8_t* codes, float* alpha_out, uint16_t* row_scale,
               int32_t* d_status, void* stream);
 
 /*
@@ -216,6 +221,25 @@ int rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float z
 int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
               const float* table, float alpha, const uint16_t* row_scale,
               const float* bias, void* y, int32_t y_dtype, void* stream);
+
+/*
+ * rb_matmul_rho_block -- rb_matmul with one row scale per block of rho_rows
+ * consecutive rows (Route B paper, section 8.2: per-head prosody, one rho
+ * per attention head whose rows share it; section 3.3's per-row scale is
+ * rho_rows = 1):
+ *
+ *     y[m, n] = alpha * rho_{n / rho_rows} * sum_k x[m, k] * table[codes[n, k]]  (+ bias[n])
+ *
+ *  row_scale  device fp16 [ceil(N / rho_rows)] or NULL (rho = 1).
+ *  rho_rows   >= 1 (TQ_ERR_SHAPE otherwise).
+ *
+ * Every other argument, the kernels and the accuracy are those of rb_matmul
+ * (which is this call with rho_rows = 1).
+ */
+int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                        const float* table, float alpha, const uint16_t* row_scale,
+                        int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
+                        void* stream);
 
 /* Human-readable name of a tq_status value. */
 const char* tq_status_string(int status);

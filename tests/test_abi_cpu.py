@@ -146,15 +146,31 @@ def test_rb_encode_argument_errors():
     assert call(6, None) == TQ_ERR_NULL                # codes
     assert call(1, -1) == TQ_ERR_SHAPE
     assert call(2, -5) == TQ_ERR_SHAPE
-    assert call(5, 2) == TQ_ERR_UNSUPPORTED            # per_row
+    assert call(5, -1) == TQ_ERR_SHAPE                 # rho_rows
     assert call(4, z(1.5)) == TQ_ERR_UNSUPPORTED       # zeta outside [0, 1]
     assert call(4, z(-0.1)) == TQ_ERR_UNSUPPORTED
     assert call(4, z(float("nan"))) == TQ_ERR_UNSUPPORTED
     assert call(3, bp) == TQ_ERR_UNSUPPORTED           # non-finite ladder step
-    assert call(5, 1) == TQ_ERR_NULL                   # per-row scales without row_scale
-    assert call(8, FAKE) == TQ_ERR_SHAPE               # row_scale without per_row
+    assert call(5, 1) == TQ_ERR_NULL                   # row scales without row_scale
+    assert call(5, 256) == TQ_ERR_NULL                 # head scales without row_scale
+    assert call(8, FAKE) == TQ_ERR_SHAPE               # row_scale with the global scale
     assert call(0, FAKE_ODD) == TQ_ERR_ALIGN
     assert call(7, FAKE_ODD) == TQ_ERR_ALIGN
+
+
+def test_rb_matmul_rho_block_argument_errors():
+    f = lib.rb_matmul_rho_block
+    ok = [FAKE, 4, 64, FAKE, 8, FAKE, ctypes.c_float(0.02), FAKE, 2, None, FAKE, 0, None]
+    bad = list(ok); bad[8] = 0
+    assert f(*bad) == TQ_ERR_SHAPE                     # rho_rows < 1
+    bad = list(ok); bad[8] = -3
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[7] = FAKE_ODD
+    assert f(*bad) == TQ_ERR_ALIGN
+    bad = list(ok); bad[5] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[1] = 0
+    assert f(*bad) == 0                                # M = 0: no-op
 
 
 def test_binding_refuses_wrong_tensors():

@@ -602,20 +602,26 @@ S0_LADDER = np.array([1, 1 / 3, 1 / 9, 1 / 27, 1 / 81], np.float32)
 S_LADDER = np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32)
 
 
-def encode_case(dmm, W, ladder, zeta=0.0, per_row=False):
-    """rb_encode on the device, bit for bit against the oracle's encoder."""
+def encode_case(dmm, W, ladder, zeta=0.0, per_row=False, rho_rows=None):
+    """rb_encode on the device, bit for bit against the oracle's encoder
+    (codes, alpha, block scales, rho)."""
     N, K = W.shape
-    say(f"rb_encode N={N} K={K} zeta={zeta} per_row={per_row}")
+    b = (1 if per_row else 0) if rho_rows is None else rho_rows
+    nb = -(-N // b) if b > 0 else 0
+    say(f"rb_encode N={N} K={K} zeta={zeta} rho_rows={b}")
     codes = torch.empty((N, K), dtype=torch.uint8, device=DEV)
-    alpha = torch.empty(1, dtype=torch.float32, device=DEV)
-    rs = torch.empty(N, dtype=torch.float16, device=DEV) if per_row else None
-    st = dmm.rb_encode(dev(W), ladder, codes, alpha, zeta=zeta, row_scale=rs)
+    alpha = torch.empty(1 + nb, dtype=torch.float32, device=DEV)
+    rs = torch.empty(nb, dtype=torch.float16, device=DEV) if b > 0 else None
+    st = dmm.rb_encode(dev(W), ladder, codes, alpha, zeta=zeta, row_scale=rs,
+                       rho_rows=b if b > 0 else None)
     assert int(host(st)[0]) == 0
-    c_ref, a_ref, r_ref = oracle.rb_encode(W, ladder, zeta=zeta, per_row=per_row)
+    c_ref, a_ref, r_ref = oracle.rb_encode(W, ladder, zeta=zeta, rho_rows=b)
     got = host(codes)
     assert np.array_equal(got, c_ref), f"{int(np.count_nonzero(got != c_ref))} codes differ"
-    assert host(alpha).view(np.uint32)[0] == np.float32(a_ref).view(np.uint32)
-    if per_row:
+    a_got = host(alpha).view(np.uint32)
+    assert a_got[0] == np.float32(a_ref).view(np.uint32)
+    if b > 0:
+        assert np.array_equal(a_got[1:], oracle.rb_block_scales(W, b).view(np.uint32))
         assert np.array_equal(host(rs.view(torch.int16)).view(np.uint16), r_ref)
     return codes, alpha, rs
 
@@ -645,6 +651,8 @@ def test_rb_encode_shapes(dmm, N, K):
             encode_case(dmm, W, lad, zeta=0.0, per_row=per_row)
     encode_case(dmm, W, S_LADDER, zeta=0.8, per_row=True)
     encode_case(dmm, W, S0_LADDER, zeta=1.0, per_row=False)
+    for b in (2, 16, N + 3):                         # head blocks, one ragged, one oversized
+        encode_case(dmm, W, S_LADDER, rho_rows=b)
 
 
 def test_rb_encode_worked_examples_and_ties(dmm):
@@ -665,14 +673,14 @@ def test_rb_encode_zero_rows_empty_and_bad_values(dmm):
     encode_case(dmm, W, S_LADDER, per_row=True)
     encode_case(dmm, np.zeros((3, 5), np.float32), S_LADDER, per_row=True)
     # K = 0: alpha = 0, rho = 0 for every row; N = 0: only alpha
-    alpha = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
+    alpha = torch.full((5,), 7.0, dtype=torch.float32, device=DEV)
     rs = torch.full((4,), 1.0, dtype=torch.float16, device=DEV)
     say("rb_encode K=0")
     dmm.rb_encode(torch.empty((4, 0), dtype=torch.float32, device=DEV), S_LADDER,
                   torch.empty((4, 0), dtype=torch.uint8, device=DEV), alpha, row_scale=rs)
-    assert float(host(alpha)[0]) == 0.0 and np.all(host(rs.view(torch.int16)) == 0)
+    assert np.all(host(alpha) == 0.0) and np.all(host(rs.view(torch.int16)) == 0)
     say("rb_encode N=0")
-    alpha.fill_(7.0)
+    alpha = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
     dmm.rb_encode(torch.empty((0, 8), dtype=torch.float32, device=DEV), S_LADDER,
                   torch.empty((0, 8), dtype=torch.uint8, device=DEV), alpha)
     assert float(host(alpha)[0]) == 0.0
@@ -680,6 +688,7 @@ def test_rb_encode_zero_rows_empty_and_bad_values(dmm):
         W2 = encode_inputs(5, 33, seed=9)
         W2[3, 7] = bad
         codes = torch.empty((5, 33), dtype=torch.uint8, device=DEV)
+        alpha = torch.empty(1, dtype=torch.float32, device=DEV)
         say(f"rb_encode non-finite {bad}")
         st = dmm.rb_encode(dev(W2), S_LADDER, codes, alpha)
         assert int(host(st)[0]) & 1
@@ -701,6 +710,49 @@ def test_rb_encode_then_matmul(dmm):
     w = oracle.rb_weights(c_ref, table, a_ref, r_ref)
     y_ref, B = oracle.matmul_ref(xb, w)
     assert_bound(y_host(y), y_ref, B, "encode then matmul")
+
+
+@pytest.mark.parametrize("M", [3, 40])
+def test_rb_encode_heads_then_matmul(dmm, M):
+    """Section 8.2 per-head prosody end to end: encode with one scale per
+    block of 64 rows (a ragged last head), then rb_matmul with rho_rows = 64
+    on the GEMV (M = 3) and prefill (M = 40) paths, against the oracle's
+    W_hat with rho_{n // 64}."""
+    N, K, b = 300, 512, 64
+    W = encode_inputs(N, K, seed=50 + M)
+    rng = np.random.default_rng(51)
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    codes, alpha, rs = encode_case(dmm, W, S_LADDER, rho_rows=b)
+    table = oracle.rb_table(S_LADDER)
+    a = float(host(alpha)[0])
+    bs = rng.standard_normal(N).astype(np.float32)
+    for ydt in (torch.float32, torch.bfloat16):
+        y = torch.empty((M, N), dtype=ydt, device=DEV)
+        say(f"rb_matmul rho_rows={b} M={M} y={ydt}")
+        dmm.rb_matmul(dev(bits16(xb)), codes, dev(table), np.float32(a), y, rs, dev(bs),
+                      rho_rows=b)
+        c_ref, a_ref, r_ref = oracle.rb_encode(W, S_LADDER, rho_rows=b)
+        w = oracle.rb_weights(c_ref, table, a_ref, r_ref, rho_rows=b)
+        y_ref, B = oracle.matmul_ref(xb, w, bs)
+        assert_bound(y_host(y), y_ref, B, f"heads M={M}", stored_of(y))
+
+
+def test_rb_matmul_rho_block_tiled_gemv(dmm):
+    """Block scales on the tiled GEMV path (K % 512 == 0, aligned): random
+    fp16 head scales for blocks of 256 rows, N = 1000 (ragged last head)."""
+    N, K, M, b = 1000, 1024, 2, 256
+    rng = np.random.default_rng(52)
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    table = oracle.rb_table(S_LADDER)
+    rho = rng.uniform(0.05, 1.0, -(-N // b)).astype(np.float16).view(np.uint16)
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    say("rb_matmul tiled rho_rows=256")
+    dmm.rb_matmul(dev(bits16(xb)), dev(codes), dev(table), np.float32(0.02), y,
+                  dev(bits16(rho)), rho_rows=b)
+    w = oracle.rb_weights(codes, table, np.float32(0.02), rho, rho_rows=b)
+    y_ref, B = oracle.matmul_ref(xb, w)
+    assert_bound(y_host(y), y_ref, B, "tiled rho_rows")
 
 
 def test_rb_encode_large(dmm):
