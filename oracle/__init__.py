@@ -50,6 +50,7 @@ from .matmul import (
     matmul_ref,
     ternary_weights,
     grouped_ref,
+    hot_prefix_weights,
     check_bound,
 )
 
@@ -58,5 +59,6 @@ __all__ = [
     "OracleDataError", "bytes_per_group", "bits_per_weight", "quantize", "pack",
     "unpack", "quantize_pack", "two_plane",
     "code_words", "rb_block_scales", "rb_encode", "rb_table", "rb_weights",
-    "REL_BOUND", "matmul_ref", "ternary_weights", "grouped_ref", "check_bound",
+    "REL_BOUND", "matmul_ref", "ternary_weights", "grouped_ref", "hot_prefix_weights",
+    "check_bound",
 ]

@@ -67,6 +67,20 @@ def grouped_ref(x_bits, expert_ids, weights_of):
     return y, B
 
 
+def hot_prefix_weights(K, G, N, n_hot, codes1, scales1, codes2=None, scales2=None):
+    """weights_of(e) for experts stored hot-first (FUCINA README, "The
+    method": hot experts get both planes, cold experts one, and the second
+    plane covers the expert prefix 0 .. n_hot - 1).  codes1 / scales1 hold
+    every expert's plane 1 ([n_experts * N] rows), codes2 / scales2 the first
+    n_hot experts' plane 2 ([n_hot * N] rows)."""
+    def weights_of(e):
+        r = slice(e * N, (e + 1) * N)
+        if e < n_hot:
+            return ternary_weights(K, G, codes1[r], scales1[r], codes2[r], scales2[r])
+        return ternary_weights(K, G, codes1[r], scales1[r])
+    return weights_of
+
+
 def bf16_half_spacing(v):
     """Half the distance between neighbouring bf16 values around |v|:
     2^(e-8) for 2^e <= |v| < 2^(e+1) (8 significant bits), 2^-134 below the

@@ -728,3 +728,33 @@ def test_encode_head_blocks():
     per_row_rho = np.repeat(rho, b)[:N]
     assert np.array_equal(oracle.rb_weights(codes, T, alpha, rho, rho_rows=b),
                           oracle.rb_weights(codes, T, alpha, per_row_rho))
+
+
+def test_hot_prefix_weights():
+    """FUCINA "The method": with the hot prefix covering every expert the
+    experts are the two-plane sums, with an empty prefix the single planes,
+    and in between expert e has its second plane exactly when e < n_hot;
+    each expert's W_hat is also re-derived from the planes' exact rationals
+    on one row."""
+    rng = np.random.default_rng(105)
+    E, N, K, G = 4, 3, 128, 64
+    W = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    (c1, s1), (c2, s2) = oracle.two_plane(W, G)
+    for n_hot in range(E + 1):
+        w_of = oracle.hot_prefix_weights(K, G, N, n_hot, c1, s1, c2[:n_hot * N], s2[:n_hot * N])
+        for e in range(E):
+            r = slice(e * N, (e + 1) * N)
+            one = oracle.ternary_weights(K, G, c1[r], s1[r])
+            two = oracle.ternary_weights(K, G, c1[r], s1[r], c2[r], s2[r])
+            assert np.array_equal(w_of(e), two if e < n_hot else one)
+    # one row by hand: trits times the fp16 scales, summed as fractions
+    w_of = oracle.hot_prefix_weights(K, G, N, 1, c1, s1, c2[:N], s2[:N])
+    t1 = oracle.unpack(c1[:1], np.full_like(s1[:1], 0x3c00), K, G)   # scale 1.0: the trits
+    t2 = oracle.unpack(c2[:1], np.full_like(s2[:1], 0x3c00), K, G)
+    sc1 = oracle.f16_bits_to_f64(s1[0])
+    sc2 = oracle.f16_bits_to_f64(s2[0])
+    for k in range(K):
+        g = k // G
+        exact = Fraction(float(t1[0, k])) * Fraction(float(sc1[g])) + \
+            Fraction(float(t2[0, k])) * Fraction(float(sc2[g]))
+        assert Fraction(float(w_of(0)[0, k])) == exact
