@@ -370,7 +370,20 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         rec = _rec(b, sec, 16, 2 * 16 * 8 * 2048 * 4096)
         rec["touched_experts"] = touched
         res["moe_two_plane_T16"] = rec
-        del pk
+        # the same experts stored hot-first: plane 2 for experts 0 .. 15 only
+        n_hot = 16
+        hot = [(p[0], p[1], p[2][:n_hot * 2048], p[3][:n_hot * 2048]) for p in pk]
+        fn = lambda: [dmm.tq_matmul_hot(x, hot[i][0], hot[i][1], 2048, 64, ys[i], n_hot, 64, ids,
+                                        8, hot[i][2], hot[i][3]) for i in range(3)]
+        sec = _timed_launches(torch, fn, 3, use_graph)
+        used = set(d["ids"].reshape(-1).tolist())
+        planes = sum(2 if e < n_hot else 1 for e in used)
+        b = planes * 2048 * 64 * 15 + 16 * 4096 * 2 + 16 * 8 * 4 + 16 * 8 * 2048 * 2
+        rec = _rec(b, sec, 16, 2 * 16 * 8 * 2048 * 4096)
+        rec["touched_experts"] = touched
+        rec["hot_experts"] = n_hot
+        res["moe_hot_prefix16_T16"] = rec
+        del pk, hot
 
     if "encode" in sel:
         progress("extra: routeb_encode")

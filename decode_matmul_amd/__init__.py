@@ -26,8 +26,8 @@ TQ_DATA_RANGE = 1
 TQ_DATA_CODE = 2
 TQ_DATA_PADDING = 4
 
-EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul",
-           "rb_matmul_rho_block", "tq_status_string")
+EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
+           "rb_matmul", "rb_matmul_rho_block", "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -44,6 +44,8 @@ _lib.tq_pack.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p]
 _lib.tq_unpack.argtypes = [_p, _p, _i64, _i64, _i32, _p, _i32, _p, _p]
 _lib.tq_matmul.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i64, _i32, _i32, _p, _i32, _p,
                            _i32, _p]
+_lib.tq_matmul_hot.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i32, _i64, _i32, _i32, _p,
+                               _i32, _p, _i32, _p]
 _lib.rb_table.argtypes = [_p, _p]
 _lib.rb_encode.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, _i32, _p, _p, _p, _p, _p]
 _lib.rb_matmul.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _p, _p, _i32, _p]
@@ -51,8 +53,8 @@ _lib.rb_matmul_rho_block.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_floa
                                      _p, _i32, _p]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
-for _name in ("tq_pack", "tq_unpack", "tq_matmul", "rb_table", "rb_encode", "rb_matmul",
-              "rb_matmul_rho_block"):
+for _name in ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
+              "rb_matmul", "rb_matmul_rho_block"):
     getattr(_lib, _name).restype = _i32
 
 
@@ -171,6 +173,27 @@ def tq_matmul(x, codes1, scales1, N, G, y, codes2=None, scales2=None, n_experts=
                         N, G, n_experts, _ptr(expert_ids), top_k, _ptr(y), _ydtype(y),
                         _stream(dev))
     _raise(rc, "tq_matmul")
+
+
+def tq_matmul_hot(x, codes1, scales1, N, G, y, n_hot, n_experts, expert_ids, top_k,
+                  codes2=None, scales2=None):
+    """Grouped experts whose plane 2 covers only the hot prefix 0 .. n_hot - 1:
+    codes2 / scales2 hold n_hot experts' second planes."""
+    dev = x.device
+    M, K = x.shape
+    cs, ss = packed_shape(N, K, G)
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes1, "codes1", _U8, n_experts * cs[0] * cs[1] * cs[2], dev)
+    _need(scales1, "scales1", _H16, n_experts * ss[0] * ss[1], dev)
+    if n_hot > 0:
+        _need(codes2, "codes2", _U8, n_hot * cs[0] * cs[1] * cs[2], dev)
+        _need(scales2, "scales2", _H16, n_hot * ss[0] * ss[1], dev)
+    _need(expert_ids, "expert_ids", _I32, M * top_k, dev)
+    _need(y, "y", (y.dtype,), M * top_k * N, dev)
+    rc = _lib.tq_matmul_hot(_ptr(x), M, K, _ptr(codes1), _ptr(scales1), _ptr(codes2),
+                            _ptr(scales2), n_hot, N, G, n_experts, _ptr(expert_ids), top_k,
+                            _ptr(y), _ydtype(y), _stream(dev))
+    _raise(rc, "tq_matmul_hot")
 
 
 def rb_table(ladder):

@@ -87,10 +87,13 @@ int tq_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_
     return hip_status(dmm::launch_unpack(codes, scales, rows, K, G, W_out, out_dtype, d_status, s));
 }
 
-int tq_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
-              const uint16_t* scales1, const uint8_t* codes2, const uint16_t* scales2,
-              int64_t N, int32_t G, int32_t n_experts, const int32_t* expert_ids,
-              int32_t top_k, void* y, int32_t y_dtype, void* stream) {
+// tq_matmul and tq_matmul_hot: n_hot < 0 gives every expert the planes
+// passed; 0 <= n_hot <= n_experts gives plane 2 to experts 0 .. n_hot - 1.
+static int tq_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
+                            const uint16_t* scales1, const uint8_t* codes2,
+                            const uint16_t* scales2, int32_t n_hot, int64_t N, int32_t G,
+                            int32_t n_experts, const int32_t* expert_ids, int32_t top_k, void* y,
+                            int32_t y_dtype, void* stream) {
     if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
         return TQ_ERR_SHAPE;
     if (!group_ok(G)) return TQ_ERR_UNSUPPORTED;
@@ -126,7 +129,51 @@ int tq_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
     a.top_k = n_experts > 0 ? top_k : 1;
     a.y = y;
     a.y_dtype = y_dtype;
-    return hip_status(dmm::launch_tq_matmul(a, (hipStream_t)stream));
+    a.e_begin = 0;
+    a.e_end = n_experts;
+    a.nan_rows = true;
+    hipStream_t s = (hipStream_t)stream;
+    if (n_hot < 0 || n_hot == n_experts) return hip_status(dmm::launch_tq_matmul(a, s));
+    if (n_hot == 0) {
+        a.planes = 1;
+        a.codes[1] = nullptr;
+        a.scales[1] = nullptr;
+        return hip_status(dmm::launch_tq_matmul(a, s));
+    }
+    // hot prefix: experts 0 .. n_hot - 1 with both planes, the rest with one
+    // (disjoint output slots; the cold launch writes the rows of invalid ids)
+    dmm::TqMatmulArgs hot = a;
+    hot.e_end = n_hot;
+    hot.nan_rows = false;
+    hipError_t e = dmm::launch_tq_matmul(hot, s);
+    if (e != hipSuccess) return TQ_ERR_HIP;
+    dmm::TqMatmulArgs cold = a;
+    cold.planes = 1;
+    cold.codes[1] = nullptr;
+    cold.scales[1] = nullptr;
+    cold.e_begin = n_hot;
+    return hip_status(dmm::launch_tq_matmul(cold, s));
+}
+
+int tq_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
+              const uint16_t* scales1, const uint8_t* codes2, const uint16_t* scales2,
+              int64_t N, int32_t G, int32_t n_experts, const int32_t* expert_ids,
+              int32_t top_k, void* y, int32_t y_dtype, void* stream) {
+    return tq_matmul_common(x, M, K, codes1, scales1, codes2, scales2, -1, N, G, n_experts,
+                            expert_ids, top_k, y, y_dtype, stream);
+}
+
+int tq_matmul_hot(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
+                  const uint16_t* scales1, const uint8_t* codes2, const uint16_t* scales2,
+                  int32_t n_hot, int64_t N, int32_t G, int32_t n_experts,
+                  const int32_t* expert_ids, int32_t top_k, void* y, int32_t y_dtype,
+                  void* stream) {
+    if (n_experts < 1) return TQ_ERR_UNSUPPORTED;     // grouped calls only
+    if (n_hot < 0 || n_hot > n_experts) return TQ_ERR_SHAPE;
+    if (n_hot > 0 && (!codes2 || !scales2)) return TQ_ERR_NULL;
+    if (n_hot == 0 && (codes2 || scales2)) return TQ_ERR_SHAPE;
+    return tq_matmul_common(x, M, K, codes1, scales1, codes2, scales2, n_hot, N, G, n_experts,
+                            expert_ids, top_k, y, y_dtype, stream);
 }
 
 int rb_table(const float* ladder, float* table_out) {

@@ -103,6 +103,8 @@ struct TqMatmulArgs {
     int planes;
     int G;
     int n_experts;          // 0 = dense
+    int e_begin, e_end;     // grouped: the experts this launch computes
+    bool nan_rows;          // grouped: this launch writes the rows of invalid ids
     const int32_t* ids;     // [M, top_k] when grouped
     int top_k;
     void* y;

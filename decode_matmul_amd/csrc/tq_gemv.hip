@@ -48,6 +48,7 @@ struct Params {
     int64_t code_stride;             // bytes per expert
     int64_t scale_stride;            // scales per expert
     int grouped;
+    int e_begin;                     // grouped: first expert of this launch
     const int32_t* ids;
     int top_k;
     int M;                           // tokens
@@ -162,7 +163,7 @@ tq_gemv_kernel(Params p) {
 
     const int item = blockIdx.x;
     const int rb = item % p.row_blocks;
-    const int e = item / p.row_blocks;
+    const int e = p.e_begin + item / p.row_blocks;
 
     if (p.grouped && wave == 0) {
         int count = 0;
@@ -386,7 +387,8 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
     p.row_blocks = (int)((a.N + 15) / 16);
     p.y = a.y;
     p.y_dtype = a.y_dtype;
-    const int experts = p.grouped ? a.n_experts : 1;
+    p.e_begin = p.grouped ? a.e_begin : 0;
+    const int experts = p.grouped ? a.e_end - a.e_begin : 1;
     const int64_t items = (int64_t)p.row_blocks * experts;
     if (items == 0) return hipSuccess;
     {
@@ -394,7 +396,7 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
         hipError_t e;
         if (launch_tq_rows(a, s, &e)) return e;
     }
-    if (p.grouped) {
+    if (p.grouped && a.nan_rows) {
         // slots routed to no valid expert: NaN rows (no expert kernel writes them)
         const int total = (int)(a.M * a.top_k);
         hipLaunchKernelGGL(bad_ids_kernel, dim3(total), dim3(256), 0, s, a.ids, total,

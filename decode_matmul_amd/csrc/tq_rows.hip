@@ -66,8 +66,10 @@ struct RowsParams {
     int total;               // T * top_k
     int top_k;
     int chunks;              // workgroups per expert
-    int n_experts;           // the workgroup after the last expert's writes the
-                             // NaN rows of slots routed to no valid expert
+    int n_experts;           // ids outside [0, n_experts) are invalid
+    int e_begin;             // first expert of this launch
+    int n_items;             // workgroups of expert rows (n_launched * chunks); one
+                             // more, when present, writes the NaN rows of invalid ids
     int64_t e_codes, e_scales;   // bytes per expert in a code / scale plane
 };
 
@@ -140,7 +142,7 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     const int lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
     if constexpr (GR) {
-        if ((int)blockIdx.x == p.n_experts * p.chunks) {
+        if ((int)blockIdx.x == p.n_items) {
             // slots whose expert id is out of range: NaN rows
             for (int i = 0; i < p.total; ++i) {
                 const int ei = p.ids[i];
@@ -155,8 +157,9 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         }
     }
     // work item: the row range, and (grouped) the expert
-    const int e = GR ? (int)blockIdx.x / p.chunks : 0;
-    const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x - e * p.chunks : (int)blockIdx.x) * p.rows_per_wg;
+    const int el = GR ? (int)blockIdx.x / p.chunks : 0;     // expert within the launch
+    const int e = GR ? p.e_begin + el : 0;
+    const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x - el * p.chunks : (int)blockIdx.x) * p.rows_per_wg;
     const int64_t r1 = min(r0 + (int64_t)p.rows_per_wg, p.N);
     const int64_t rlast = r1 - 1;
     const int nb = (int)((r1 - r0 + 15) >> 4);
@@ -459,11 +462,19 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.top_k = a.top_k;
     p.chunks = (int)((a.N + rpw - 1) / rpw);
     p.n_experts = grouped ? a.n_experts : 0;
+    p.e_begin = grouped ? a.e_begin : 0;
     p.e_codes = a.N * ng * kNB;
     p.e_scales = a.N * ng * 2;
-    // grouped: one more workgroup for the slots routed to no valid expert
-    const int64_t wgs = grouped ? (int64_t)a.n_experts * p.chunks + 1 : p.chunks;
+    // grouped: the launch's experts, and one more workgroup for the slots
+    // routed to no valid expert when this launch writes them
+    const int64_t items = grouped ? (int64_t)(a.e_end - a.e_begin) * p.chunks : p.chunks;
+    const int64_t wgs = items + ((grouped && a.nan_rows) ? 1 : 0);
     if (wgs >= (1ll << 31)) return false;
+    if (wgs == 0) {
+        *err = hipSuccess;
+        return true;
+    }
+    p.n_items = (int)items;
     const dim3 grid((unsigned)wgs), block(kT);
 #define DMM_ROWS(PL_, SPB_)                                                                \
     do {                                                                                   \

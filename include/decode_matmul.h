@@ -142,6 +142,31 @@ int tq_matmul(const uint16_t* x, int64_t M, int64_t K,
               int32_t top_k, void* y, int32_t y_dtype, void* stream);
 
 /*
+ * tq_matmul_hot -- grouped two-plane experts with a hot prefix (FUCINA
+ * README, "The method": hot experts get both planes and cold experts one,
+ * and experts are stored hot-first so that the second plane covers the
+ * expert prefix 0 .. n_hot - 1; "Runtime requirements": the second-plane
+ * tensors hold their own expert count):
+ *
+ *     y[t, j, :] = x[t] (s1 T1_e + [e < n_hot] s2 T2_e)^T,  e = expert_ids[t, j]
+ *
+ *  codes1, scales1  plane 1 of all n_experts experts, as in tq_matmul.
+ *  codes2, scales2  plane 2 of experts 0 .. n_hot - 1 only (same per-expert
+ *                   layout), NULL when n_hot = 0.
+ *  n_hot            0 <= n_hot <= n_experts; the count is an argument, never
+ *                   inferred from the buffers.
+ *
+ * Grouped calls only (n_experts >= 1, else TQ_ERR_UNSUPPORTED); every other
+ * argument, the invalid-id NaN rows and the accuracy are those of tq_matmul
+ * (n_hot = n_experts is its two-plane call, n_hot = 0 its one-plane call).
+ */
+int tq_matmul_hot(const uint16_t* x, int64_t M, int64_t K,
+                  const uint8_t* codes1, const uint16_t* scales1,
+                  const uint8_t* codes2, const uint16_t* scales2, int32_t n_hot,
+                  int64_t N, int32_t G, int32_t n_experts, const int32_t* expert_ids,
+                  int32_t top_k, void* y, int32_t y_dtype, void* stream);
+
+/*
  * rb_table -- build the 243-entry Route B code book on the host (Route B
  * paper, section 3.2: the 3^5 words of a 5-step ternary ladder are
  * enumerated once per layer).

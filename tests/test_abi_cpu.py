@@ -158,6 +158,27 @@ def test_rb_encode_argument_errors():
     assert call(7, FAKE_ODD) == TQ_ERR_ALIGN
 
 
+def test_tq_matmul_hot_argument_errors():
+    f = lib.tq_matmul_hot
+    ok = [FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, 2, 16, 64, 4, FAKE, 2, FAKE, 0, None]
+    bad = list(ok); bad[10] = 0
+    assert f(*bad) == TQ_ERR_UNSUPPORTED               # dense: not a grouped call
+    bad = list(ok); bad[7] = 5
+    assert f(*bad) == TQ_ERR_SHAPE                     # n_hot > n_experts
+    bad = list(ok); bad[7] = -1
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[5] = None
+    assert f(*bad) == TQ_ERR_NULL                      # hot experts without plane 2
+    bad = list(ok); bad[7] = 0
+    assert f(*bad) == TQ_ERR_SHAPE                     # plane 2 given for no hot expert
+    bad = list(ok); bad[9] = 96
+    assert f(*bad) == TQ_ERR_UNSUPPORTED               # group size
+    bad = list(ok); bad[11] = None
+    assert f(*bad) == TQ_ERR_NULL                      # ids
+    bad = list(ok); bad[1] = 0
+    assert f(*bad) == 0                                # M = 0: no-op
+
+
 def test_rb_matmul_rho_block_argument_errors():
     f = lib.rb_matmul_rho_block
     ok = [FAKE, 4, 64, FAKE, 8, FAKE, ctypes.c_float(0.02), FAKE, 2, None, FAKE, 0, None]

@@ -348,6 +348,40 @@ def test_tq_matmul_grouped_streaming(dmm):
     grouped_case(dmm, 4, 40, 1024, 3, 2, 1, seed=26, bad_ids="all")
 
 
+def hot_case(dmm, E, N, K, T, top_k, n_hot, seed, bad_ids=False, ydt=torch.float32):
+    """tq_matmul_hot: plane 2 only for experts 0 .. n_hot - 1."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    xb = workloads.bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    if bad_ids:
+        ids[0, 0] = -2
+        ids[T - 1, top_k - 1] = E
+    (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    c2h, s2h = c2[:n_hot * N], s2[:n_hot * N]
+    y = torch.empty((T, top_k, N), dtype=ydt, device=DEV)
+    say(f"tq_matmul_hot E={E} N={N} K={K} T={T} top_k={top_k} n_hot={n_hot} bad={bad_ids} y={ydt}")
+    dmm.tq_matmul_hot(dev(bits16(xb)), dev(c1), dev(bits16(s1)), N, 64, y, n_hot, E, dev(ids),
+                      top_k, None if n_hot == 0 else dev(c2h),
+                      None if n_hot == 0 else dev(bits16(s2h)))
+    got = y_host(y)
+    valid = (ids >= 0) & (ids < E)
+    w_of = oracle.hot_prefix_weights(K, 64, N, n_hot, c1, s1, c2h, s2h)
+    y_ref, B = oracle.grouped_ref(xb, np.where(valid, ids, 0), w_of)
+    assert_bound(got[valid], y_ref[valid], B[valid], f"hot n_hot={n_hot}", stored_of(y))
+    assert np.all(np.isnan(got[~valid]))
+
+
+@pytest.mark.parametrize("K", [256, 1024, 4096])
+def test_tq_matmul_hot_prefix(dmm, K):
+    """Hot prefixes of every size on the general (K = 256) and streaming
+    (K = 1024, 4096) forms, with invalid ids and bf16 output."""
+    E, N, T, top_k = 6, 40, 7, 3
+    for n_hot in (0, 1, 4, E):
+        hot_case(dmm, E, N, K, T, top_k, n_hot, seed=K + n_hot)
+    hot_case(dmm, E, N, K, T, top_k, 2, seed=K + 9, bad_ids=True, ydt=torch.bfloat16)
+
+
 def test_tq_grouped_equals_dense_when_one_expert(dmm):
     """Every (token, slot) routed to expert 2 gives, slot by slot, exactly the
     dense result of expert 2's package (same kernel arithmetic)."""
