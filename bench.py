@@ -339,6 +339,21 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
             b = c.numel() + s.numel() * 2 + M * 4096 * 2 + M * 14336 * 2
             res[f"ternary_gemv_M{M}"] = _rec(b, sec, M, 2 * M * 14336 * 4096)
         del cc, sc
+        # ternary prefill: the same package at M = 2048 tokens (MFMA bound)
+        progress("extra: ternary_prefill")
+        Mp = 2048
+        rng = np.random.default_rng(6)
+        xp = to_dev(bits16(workloads.bf16_bits(rng.standard_normal((Mp, 4096)).astype(np.float32))))
+        yp = torch.empty((Mp, 14336), dtype=torch.bfloat16, device=dev)
+        fn = lambda: dmm.tq_matmul(xp, c, s, 14336, 64, yp)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=5, warmup=1)
+        flops = 2.0 * Mp * 14336 * 4096
+        res["ternary_prefill_M2048"] = {
+            "us_per_launch": round(sec * 1e6, 2),
+            "tflops": round(flops / sec / 1e12, 2),
+            "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        }
+        del xp, yp
 
     if "moe" in sel:
         progress("extra: moe_two_plane (generating 2 GiB of weights)")

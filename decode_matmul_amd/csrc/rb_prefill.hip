@@ -80,32 +80,6 @@ struct Slice {
     u32x4 cd[CCH];
 };
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Running range of the activations of one chunk (bf16 bits with the sign
-// cleared, two halves per word): the largest value, and the smallest
-// nonzero value minus one (a zero wraps to 0xffff and drops out).
-struct Range {
-    u16x2 hi = {0, 0};
-    u16x2 lo = {0xffff, 0xffff};
-};
-
-// Two bf16 activations -> two fp16 (exact inside the range that R checks).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d, Range& R) {
-    const u16x2 t = __builtin_bit_cast(u16x2, d & 0x7fff7fffu);
-    R.hi = __builtin_elementwise_max(R.hi, t);
-    R.lo = __builtin_elementwise_min(R.lo, (u16x2)(t - (u16x2){1, 1}));
-    const float a = __builtin_bit_cast(float, d << 16);
-    const float b = __builtin_bit_cast(float, d & 0xffff0000u);
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-// True when every activation seen is 0 or has 2^-17 <= |x| <= 65280
-// (bf16 bits 0x3700 .. 0x477f), i.e. is exact in fp16.
-__device__ __forceinline__ bool range_ok(const Range& R) {
-    return max(R.hi.x, R.hi.y) <= 0x477f && min(R.lo.x, R.lo.y) >= 0x36ff;
-}
-
 template <bool AL>
 __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     // one LDS block: the code book at address 0 (so a v_perm result is its

@@ -395,6 +395,7 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
         // the streaming form writes the rows of out-of-range expert ids itself
         hipError_t e;
         if (launch_tq_rows(a, s, &e)) return e;
+        if (launch_tq_prefill(a, s, &e)) return e;
     }
     if (p.grouped && a.nan_rows) {
         // slots routed to no valid expert: NaN rows (no expert kernel writes them)

@@ -204,10 +204,16 @@ def test_unpack_rejects_bad_bytes(dmm):
 
 # ------------------------------------------------------------------ tq_matmul
 
-def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0):
+def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0, x_special=False):
     rng = np.random.default_rng(seed)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
-    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    if x_special:
+        # activations fp16 cannot hold (tiny, huge) in a few chunks, zeros elsewhere
+        xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = 3.0e-7
+        xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = -7.0e4
+        xf[rng.integers(0, M, 20), rng.integers(0, K, 20)] = 0.0
+    xb = workloads.bf16_bits(xf)
     if planes == 1:
         c1, s1 = oracle.quantize_pack(W, G)
         c2 = s2 = None
@@ -228,6 +234,43 @@ def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0):
     dmm.tq_matmul(xd, put_codes(c1), dev(bits16(s1)), N, G, y,
                   put_codes(c2), None if s2 is None else dev(bits16(s2)))
     return assert_bound(y_host(y), y_ref, B, f"tq M={M} N={N} K={K}", stored_of(y))
+
+
+# Shapes of the MFMA prefill form (dense, one plane, G = 64, M >= 128): one
+# K-slice, ragged M and N tiles, N below one tile, several tiles each way.
+TQ_PREFILL_CASES = [
+    (128, 256, 64), (130, 300, 128), (300, 257, 320), (256, 1000, 1024), (129, 17, 192),
+    (512, 600, 512),
+]
+
+
+@pytest.mark.parametrize("M,N,K", TQ_PREFILL_CASES)
+def test_tq_matmul_prefill_shapes(dmm, M, N, K):
+    tq_case(dmm, M, N, K, 64, 1, torch.float32, seed=M + 3 * N + K)
+    tq_case(dmm, M, N, K, 64, 1, torch.bfloat16, seed=M + 5 * N + K, x_special=True)
+
+
+def test_tq_matmul_prefill_full_sampled(dmm):
+    """ternary_gemv weights (14336 x 4096) at M = 2048 tokens: 64 sampled
+    token rows against the oracle over all 14336 outputs."""
+    d = workloads.ternary_gemv(M=1)
+    cs, ss = dmm.packed_shape(14336, 4096, 64)
+    W = dev(d["W"])
+    c = torch.empty(cs, dtype=torch.uint8, device=DEV)
+    s = torch.empty(ss, dtype=torch.int16, device=DEV)
+    say("tq_pack ternary_gemv for prefill")
+    assert int(host(dmm.tq_pack(W, 64, 1, c, s))[0]) == 0
+    del W
+    rng = np.random.default_rng(60)
+    xb = workloads.bf16_bits(rng.standard_normal((2048, 4096)).astype(np.float32))
+    y = torch.empty((2048, 14336), dtype=torch.bfloat16, device=DEV)
+    say("tq_matmul prefill M=2048 N=14336 K=4096")
+    dmm.tq_matmul(dev(bits16(xb)), c, s, 14336, 64, y)
+    rows = np.sort(rng.choice(2048, 64, replace=False))
+    got = y_host(y)[rows]
+    w = oracle.ternary_weights(4096, 64, host(c), host(s).view(np.uint16))
+    y_ref, B = oracle.matmul_ref(xb[rows], w)
+    assert_bound(got, y_ref, B, "ternary prefill sampled", "bf16")
 
 
 TQ_CASES = [
