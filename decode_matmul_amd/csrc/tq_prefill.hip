@@ -1,10 +1,12 @@
-// Ternary prefill (dense, G = 64, one plane, many tokens): y = x (s T)^T as an
-// MFMA GEMM whose weight tiles are decoded from the packed trits into LDS.
+// Ternary prefill (dense, G = 64, one or two planes, many tokens):
+// y = x (s1 T1 + s2 T2)^T as an MFMA GEMM whose weight tiles are decoded from
+// the packed trits into LDS.
 //
 // Format: "Does your weight format deserve a kernel?" (pack-unpack-run),
 // "Five trits in a byte" (trit 5i + q of a group is digit q of byte i, least
 // significant first, t = d - 1) and "Three values and a shared scale" (w =
-// s t with one fp16 s per group of 64).
+// s t with one fp16 s per group of 64); the second plane follows the FUCINA
+// README ("The method": W ~ d1 T1 + d2 T2), each plane its own K-slice.
 //
 // Numerics.  The products run on fp16 MFMAs with fp32 accumulation:
 //  * A weight s t (t in {-1, 0, +1}, s an fp16 scale) is an fp16 value, so
@@ -20,7 +22,8 @@
 //  * A 512-thread workgroup (8 waves in a 2 x 4 grid, two per SIMD) owns a
 //    128 x 256 tile of y (tokens x rows); each wave owns 64 x 64 = 2 x 2 MFMA
 //    32x32x16 tiles.
-//  * K-slices of 64 (one group) in two LDS buffers: while the MFMAs of slice s
+//  * K-slices of 64 (one group of one plane; with two planes, slice 2g + q is
+//    plane q of group g over the same activations) in two LDS buffers: while the MFMAs of slice s
 //    run, slice s + 1 (loaded from global memory an iteration earlier) is
 //    decoded into the other buffer and slice s + 2 is loaded.  One barrier per
 //    slice.
@@ -60,8 +63,11 @@ struct Params {
     const uint16_t* x;
     int64_t M, K, N;
     int ng;                        // groups per row (K / 64)
-    const uint8_t* codes;          // [N][ng][13]
-    const uint16_t* scales;        // [N][ng] fp16 bits
+    int planes;                    // 1 or 2
+    const uint8_t* codes;          // plane 1 [N][ng][13]
+    const uint16_t* scales;        // plane 1 [N][ng] fp16 bits
+    const uint8_t* codes2;         // plane 2 (planes == 2)
+    const uint16_t* scales2;
     void* y;
     int y_dtype;
 };
@@ -131,7 +137,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
 
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int nslices = p.ng;
+    const int nslices = p.ng * p.planes;
     const uint32_t cofs = (uint32_t)(lane & 15) << 4;           // >> 1 below: copy lane % 16
 
     // this thread's activation chunks (rows xr_i, 8 values at column xc) and
@@ -142,7 +148,11 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     const int64_t row_bytes = (int64_t)p.ng * kNB;
 
     auto gload = [&](int s, Slice& S) {
-        const int g = min(s, nslices - 1);
+        const int sc = min(s, nslices - 1);
+        const int g = p.planes == 2 ? sc >> 1 : sc;
+        const bool second = p.planes == 2 && (sc & 1);
+        const uint8_t* codes = second ? p.codes2 : p.codes;
+        const uint16_t* scales = second ? p.scales2 : p.scales;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int64_t m = min(m0 + xr0 + 64 * i, p.M - 1);
@@ -151,11 +161,11 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
         const int64_t off = wrow * row_bytes + (int64_t)g * kNB + 6 * H;   // 7 bytes
         const int64_t a0 = off & ~(int64_t)3;
         const int64_t a2 = (off + 6) & ~(int64_t)3;                        // word of the last byte
-        S.cw[0] = *(const uint32_t*)(p.codes + a0);
-        S.cw[1] = *(const uint32_t*)(p.codes + a0 + 4);
-        S.cw[2] = *(const uint32_t*)(p.codes + a2);
+        S.cw[0] = *(const uint32_t*)(codes + a0);
+        S.cw[1] = *(const uint32_t*)(codes + a0 + 4);
+        S.cw[2] = *(const uint32_t*)(codes + a2);
         S.sh = (uint32_t)(off & 3);
-        S.sc = p.scales[wrow * p.ng + g];
+        S.sc = scales[wrow * p.ng + g];
     };
 
     // fp16 pairs of t for this thread's 32 trits
@@ -382,14 +392,17 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
 
 }  // namespace
 
-// Dense one-plane ternary matmul for many tokens; false (nothing launched)
-// outside its domain: G = 64, one plane, M >= 128, x 16-byte and codes 4-byte
-// aligned, a grid within the launch limits.
+// Dense ternary matmul for many tokens; false (nothing launched) outside its
+// domain: G = 64, M >= 128, x 16-byte and codes 4-byte aligned, K / 64 * planes
+// slices within the LDS flag map's index range, a grid within the launch limits.
 bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
-    if (a.n_experts != 0 || a.G != 64 || a.planes != 1 || a.M < BM || a.K < BK ||
-        a.K % BK != 0 || ((uintptr_t)a.x & 15) != 0 || ((uintptr_t)a.codes[0] & 3) != 0 ||
+    if (a.n_experts != 0 || a.G != 64 || a.M < BM || a.K < BK || a.K % BK != 0 ||
+        ((uintptr_t)a.x & 15) != 0 || ((uintptr_t)a.codes[0] & 3) != 0 ||
         ((uintptr_t)a.scales[0] & 1) != 0)
         return false;
+    if (a.planes == 2 && (((uintptr_t)a.codes[1] & 3) != 0 || ((uintptr_t)a.scales[1] & 1) != 0))
+        return false;
+    if ((a.K / BK) * a.planes >= (1ll << 30)) return false;
     const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
     if (gx == 0 || gx >= (1ll << 31) || gy >= 65536) return false;
     Params p;
@@ -398,8 +411,11 @@ bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.K = a.K;
     p.N = a.N;
     p.ng = (int)(a.K / BK);
+    p.planes = a.planes;
     p.codes = a.codes[0];
     p.scales = a.scales[0];
+    p.codes2 = a.planes == 2 ? a.codes[1] : a.codes[0];
+    p.scales2 = a.planes == 2 ? a.scales[1] : a.scales[0];
     p.y = a.y;
     p.y_dtype = a.y_dtype;
     hipLaunchKernelGGL(tq_prefill_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s, p);

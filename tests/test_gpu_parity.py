@@ -236,8 +236,8 @@ def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0, x_special=F
     return assert_bound(y_host(y), y_ref, B, f"tq M={M} N={N} K={K}", stored_of(y))
 
 
-# Shapes of the MFMA prefill form (dense, one plane, G = 64, M >= 128): one
-# K-slice, ragged M and N tiles, N below one tile, several tiles each way.
+# Shapes of the MFMA prefill form (dense, one or two planes, G = 64, M >= 128):
+# one group, ragged M and N tiles, N below one tile, several tiles each way.
 TQ_PREFILL_CASES = [
     (128, 256, 64), (130, 300, 128), (300, 257, 320), (256, 1000, 1024), (129, 17, 192),
     (512, 600, 512),
@@ -248,6 +248,8 @@ TQ_PREFILL_CASES = [
 def test_tq_matmul_prefill_shapes(dmm, M, N, K):
     tq_case(dmm, M, N, K, 64, 1, torch.float32, seed=M + 3 * N + K)
     tq_case(dmm, M, N, K, 64, 1, torch.bfloat16, seed=M + 5 * N + K, x_special=True)
+    tq_case(dmm, M, N, K, 64, 2, torch.float32, seed=M + 7 * N + K)
+    tq_case(dmm, M, N, K, 64, 2, torch.bfloat16, seed=M + 9 * N + K, x_special=True)
 
 
 def test_tq_matmul_prefill_full_sampled(dmm):
