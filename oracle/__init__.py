@@ -14,8 +14,9 @@ pages it follows:
   ("Count the bytes you actually wrote").
 * "A Discrete Weight Language for Large Language Models: Compressing Gemma 4
   31B with a 5-Step Ternary Route" (Route B): the 243-word code book (section
-  3.2), the per-row scale (section 3.3) and the fused LUT matmul semantics
-  (section 4.2).
+  3.2), the per-row scale (section 3.3), the fused LUT matmul semantics
+  (section 4.2), per-head scales (section 8.2), the 7-bit truncated alphabet
+  (section 8.1) and per-block code books (section 8.3).
 * "FUCINA - a general ternary forge for Mixture-of-Experts models": the
   two-plane sum W ~ d1*T1 + d2*T2 ("The method") and the expert matmul.
 
@@ -44,7 +45,17 @@ from .ternary import (
     quantize_pack,
     two_plane,
 )
-from .routeb import code_words, rb_block_scales, rb_encode, rb_table, rb_weights
+from .routeb import (
+    code_words,
+    rb_block_scales,
+    rb_encode,
+    rb_table,
+    rb_weights,
+    rb_truncate,
+    pack7,
+    unpack7,
+    rb_weights7,
+)
 from .matmul import (
     REL_BOUND,
     matmul_ref,
@@ -59,6 +70,7 @@ __all__ = [
     "OracleDataError", "bytes_per_group", "bits_per_weight", "quantize", "pack",
     "unpack", "quantize_pack", "two_plane",
     "code_words", "rb_block_scales", "rb_encode", "rb_table", "rb_weights",
+    "rb_truncate", "pack7", "unpack7", "rb_weights7",
     "REL_BOUND", "matmul_ref", "ternary_weights", "grouped_ref", "hot_prefix_weights",
     "check_bound",
 ]

@@ -52,6 +52,25 @@ with rho_rows = b, block h = rows [h b, (h + 1) b) is normalised by its
 largest |W| (alpha_h) and rho_h = fp16(alpha_h / alpha); rho_rows = 1 is the
 per-row scale of section 3.3, and the decoded weight of row n uses
 rho_{n // b}.
+
+Adaptive alphabets (section 8.3: a ladder per block of 32 rows instead of
+one per family) decode row n through the code book of its block: with
+table_rows = b, rows [h b, (h + 1) b) read tables[h], each table built from
+its block's ladder by rb_table.  Readings: the stored form is the block's
+ladder (five fp32 steps, the size of ten fp16 numbers); alpha stays one
+per-layer scale, and the block scales rho are unchanged.
+
+The 7-bit truncated alphabet (section 8.1: when a layer uses at most 128 of
+the 243 codes, each weight is stored in 7 bits plus a table from the 7-bit
+index to the code) is rb_truncate, pack7 and unpack7.  Readings:
+
+* The used codes are listed in increasing order; index j stands for the
+  j-th smallest code that occurs in the matrix.  The list is padded to 128
+  entries with code 121 (the all-zero word, a zero weight for any ladder).
+* Row n of the packed matrix is a little-endian bit string of ceil(7 K / 8)
+  bytes: bit q of index k is bit 7 k + q of the string, and bit p of the
+  string is bit p % 8 of byte p // 8.  The bits past 7 K are zero.
+* More than 128 distinct codes, or a byte 243..255, is an error.
 """
 
 import numpy as np
@@ -78,13 +97,25 @@ def rb_table(ladder):
     return f64_to_f32(acc)
 
 
-def rb_weights(codes, table, alpha, row_scale_bits=None, rho_rows=1):
+def rb_weights(codes, table, alpha, row_scale_bits=None, rho_rows=1, table_rows=0):
     """codes uint8 [N, K] -> W_hat float64 [N, K] = alpha * T[code] * rho,
-    rho of row n being row_scale[n // rho_rows]."""
+    rho of row n being row_scale[n // rho_rows].  table_rows = 0: one code
+    book T float32 [243]; table_rows = b: tables float32 [ceil(N / b), 243]
+    and row n reads tables[n // b] (section 8.3)."""
     codes = np.asarray(codes, dtype=np.uint8)
-    t256 = np.zeros(256, dtype=np.float64)
-    t256[:243] = np.asarray(table, dtype=np.float32).astype(np.float64)
-    w = float(np.float32(alpha)) * t256[codes]
+    N = codes.shape[0]
+    tab = np.asarray(table, dtype=np.float32).astype(np.float64).reshape(-1, 243)
+    if table_rows == 0:
+        if tab.shape[0] != 1:
+            raise ValueError("one code book without table_rows")
+        block = np.zeros(N, dtype=np.int64)
+    else:
+        if tab.shape[0] != -(-N // table_rows):
+            raise ValueError("one code book per block of table_rows rows")
+        block = np.arange(N) // table_rows
+    t256 = np.zeros((tab.shape[0], 256), dtype=np.float64)
+    t256[:, :243] = tab
+    w = float(np.float32(alpha)) * t256[block[:, None], codes]
     if row_scale_bits is not None:
         rho = f16_bits_to_f64(row_scale_bits)
         w = w * rho[np.arange(codes.shape[0]) // rho_rows][:, None]
@@ -150,3 +181,53 @@ def rb_encode(W, ladder, zeta=0.0, per_row=False, rho_rows=None):
             q = blocks / alpha
         rho = f64_to_f16_bits(q)
     return codes.astype(np.uint8), np.float32(alpha), rho
+
+
+def rb_truncate(codes):
+    """Section 8.1 truncated alphabet: codes uint8 [N, K] -> (used uint8 [128],
+    n_used, index uint8 [N, K]) with used[index[n, k]] == codes[n, k]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.size and int(codes.max()) > 242:
+        raise ValueError("byte 243..255 is not a code")
+    present = np.zeros(243, dtype=bool)
+    present[codes.ravel()] = True
+    used_codes = np.flatnonzero(present)                  # increasing
+    n_used = int(used_codes.size)
+    if n_used > 128:
+        raise ValueError("more than 128 codes in use")
+    index_of = np.zeros(256, dtype=np.uint8)
+    index_of[used_codes] = np.arange(n_used)
+    used = np.full(128, 121, dtype=np.uint8)
+    used[:n_used] = used_codes
+    return used, n_used, index_of[codes]
+
+
+def pack7(index):
+    """index uint8 [N, K], each < 128 -> uint8 [N, ceil(7 K / 8)]: bit q of
+    index k is bit 7 k + q of the row's little-endian bit string."""
+    index = np.asarray(index, dtype=np.uint8)
+    if index.size and int(index.max()) > 127:
+        raise ValueError("a 7-bit index is below 128")
+    N, K = index.shape
+    L = -(-7 * K // 8)
+    bits = (index[:, :, None] >> np.arange(7, dtype=np.uint8)) & 1     # [N, K, 7]
+    stream = np.zeros((N, 8 * L), dtype=np.uint8)
+    stream[:, :7 * K] = bits.reshape(N, 7 * K)
+    return np.packbits(stream, axis=1, bitorder="little")
+
+
+def unpack7(packed, K):
+    """Inverse of pack7: uint8 [N, ceil(7 K / 8)] -> index uint8 [N, K]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    if packed.shape[1] != -(-7 * K // 8):
+        raise ValueError("ceil(7 K / 8) bytes per row")
+    bits = np.unpackbits(packed, axis=1, bitorder="little")[:, :7 * K].reshape(N, K, 7)
+    return (bits.astype(np.uint32) << np.arange(7, dtype=np.uint32)).sum(axis=2).astype(np.uint8)
+
+
+def rb_weights7(packed, K, used, table, alpha, row_scale_bits=None, rho_rows=1, table_rows=0):
+    """W_hat of a 7-bit packed matrix: the code of weight (n, k) is
+    used[index[n, k]], then rb_weights."""
+    codes = np.asarray(used, dtype=np.uint8)[unpack7(packed, K)]
+    return rb_weights(codes, table, alpha, row_scale_bits, rho_rows, table_rows)

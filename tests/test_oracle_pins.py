@@ -758,3 +758,138 @@ def test_hot_prefix_weights():
         exact = Fraction(float(t1[0, k])) * Fraction(float(sc1[g])) + \
             Fraction(float(t2[0, k])) * Fraction(float(sc2[g]))
         assert Fraction(float(w_of(0)[0, k])) == exact
+
+
+# ------------------------------------------- Route B sections 8.1 and 8.3
+
+def _pack7_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "routeb_pack7_example.txt")
+    cases = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            left, right = line.split(":")
+            nums = [int(v) for v in left.split()]
+            K, idx = nums[0], nums[1:]
+            assert len(idx) == K
+            cases.append((K, idx, [int(v, 16) for v in right.split()]))
+    return cases
+
+
+def test_pack7_worked_example():
+    """Section 8.1: 7-bit indices, packed bytes worked out by hand."""
+    cases = _pack7_golden()
+    assert len(cases) == 4
+    for K, idx, want in cases:
+        got = oracle.pack7(np.array([idx], np.uint8))
+        assert got.shape == (1, -(-7 * K // 8))
+        assert list(got[0]) == want
+        assert list(oracle.unpack7(got, K)[0]) == idx
+
+
+def test_pack7_single_bits():
+    """One set bit q of index k lands on stream bit 7k + q, i.e. byte
+    (7k+q) // 8, bit (7k+q) % 8; every other bit is zero."""
+    for K in (1, 7, 8, 9, 33):
+        for k in range(K):
+            for q in range(7):
+                idx = np.zeros((1, K), np.uint8)
+                idx[0, k] = 1 << q
+                got = oracle.pack7(idx)[0]
+                p = 7 * k + q
+                want = np.zeros(-(-7 * K // 8), np.uint8)
+                want[p // 8] = 1 << (p % 8)
+                assert np.array_equal(got, want), (K, k, q)
+
+
+def test_pack7_round_trip_and_padding():
+    rng = np.random.default_rng(81)
+    for K in (1, 5, 8, 64, 100, 1024):
+        idx = rng.integers(0, 128, (3, K), dtype=np.uint8)
+        packed = oracle.pack7(idx)
+        assert packed.shape == (3, -(-7 * K // 8))
+        assert np.array_equal(oracle.unpack7(packed, K), idx)
+        ones = oracle.pack7(np.full((1, K), 127, np.uint8))[0]
+        bits = np.unpackbits(ones, bitorder="little")
+        assert bits[:7 * K].all() and not bits[7 * K:].any()
+    with pytest.raises(ValueError):
+        oracle.pack7(np.array([[128]], np.uint8))
+
+
+def test_truncate_alphabet():
+    """Section 8.1: the used codes in increasing order, used[index] == codes,
+    the list padded with the all-zero word 121, at most 128 codes."""
+    rng = np.random.default_rng(82)
+    alphabet = np.sort(rng.choice(243, 45, replace=False)).astype(np.uint8)
+    codes = alphabet[rng.integers(0, 45, (40, 70))]
+    codes[0, :45] = alphabet                        # every letter occurs
+    used, n_used, index = oracle.rb_truncate(codes)
+    assert n_used == 45
+    assert np.array_equal(used[:45], alphabet)
+    assert (used[45:] == 121).all()
+    assert np.array_equal(used[index], codes)
+    assert int(index.max()) == 44
+    # one code; an empty matrix; all 128; too many; a non-code byte
+    u1, n1, i1 = oracle.rb_truncate(np.full((2, 3), 200, np.uint8))
+    assert n1 == 1 and u1[0] == 200 and (i1 == 0).all()
+    u0, n0, _ = oracle.rb_truncate(np.zeros((0, 4), np.uint8))
+    assert n0 == 0 and (u0 == 121).all()
+    c128 = np.arange(115, 243).astype(np.uint8)[None, :]
+    u, n, i = oracle.rb_truncate(c128)
+    assert n == 128 and np.array_equal(u, c128[0]) and np.array_equal(i[0], np.arange(128))
+    with pytest.raises(ValueError):
+        oracle.rb_truncate(np.arange(114, 243).astype(np.uint8)[None, :])
+    with pytest.raises(ValueError):
+        oracle.rb_truncate(np.array([[3, 250]], np.uint8))
+
+
+def test_rb_weights7_decodes_through_used_codes():
+    """The 7-bit form decodes to the same weights as the code bytes, and an
+    index past n_used (code 121) is a zero weight for any ladder."""
+    rng = np.random.default_rng(83)
+    lad = workloads_ladder(rng)
+    T = oracle.rb_table(lad)
+    assert T[121] == 0.0
+    codes = rng.choice(np.array([3, 40, 121, 150, 202, 242], np.uint8), (6, 50))
+    used, n_used, index = oracle.rb_truncate(codes)
+    packed = oracle.pack7(index)
+    rho = np.array([0.5, 1.0, 1.25, 0.75, 1.5, 2.0], np.float16).view(np.uint16)
+    assert np.array_equal(oracle.rb_weights7(packed, 50, used, T, np.float32(0.02), rho),
+                          oracle.rb_weights(codes, T, np.float32(0.02), rho))
+    pad = np.full((1, 8), 100, np.uint8)             # index 100 >= n_used
+    assert (oracle.rb_weights7(oracle.pack7(pad), 8, used, T, np.float32(1)) == 0).all()
+
+
+def workloads_ladder(rng):
+    u = rng.uniform(0.8, 1.2, 5).astype(np.float32)
+    return (np.float32(0.5) ** np.arange(5, dtype=np.float32) * u).astype(np.float32)
+
+
+def test_block_tables_closed_form():
+    """Section 8.3: rows of block h read code book h.  Under the integer
+    ladder (81, 27, 9, 3, 1) scaled by 2^h, T_h[b] = 2^h (b - 121) exactly,
+    so every weight is alpha 2^(n // 32) (code - 121); a ragged last block
+    works; equal tables reduce to the one-table call; swapping two blocks of
+    rows together with their tables swaps the rows."""
+    base = np.array([81, 27, 9, 3, 1], np.float32)
+    N, K, b = 70, 9, 32                                  # blocks of 32, 32, 6 rows
+    nb = 3
+    tables = np.stack([oracle.rb_table(base * np.float32(2.0 ** h)) for h in range(nb)])
+    for h in range(nb):
+        assert np.array_equal(tables[h], (2.0 ** h * (np.arange(243) - 121)).astype(np.float32))
+    rng = np.random.default_rng(84)
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    alpha = np.float32(0.375)
+    w = oracle.rb_weights(codes, tables, alpha, table_rows=b)
+    want = 0.375 * 2.0 ** (np.arange(N) // b)[:, None] * (codes.astype(np.float64) - 121)
+    assert np.array_equal(w, want)
+    same = np.stack([tables[1]] * nb)
+    assert np.array_equal(oracle.rb_weights(codes, same, alpha, table_rows=b),
+                          oracle.rb_weights(codes, tables[1], alpha))
+    perm = np.r_[np.arange(32, 64), np.arange(0, 32), np.arange(64, 70)]
+    w_sw = oracle.rb_weights(codes[perm], tables[[1, 0, 2]], alpha, table_rows=b)
+    assert np.array_equal(w_sw, w[perm])
+    with pytest.raises(ValueError):
+        oracle.rb_weights(codes, tables[:2], alpha, table_rows=b)

@@ -21,6 +21,18 @@ configuration's index as the seed, in the order written below.
   routeb_prefill Route B prefill: codes uint8 8192x8192 as routeb_gemv,
                  ladder as routeb_gemv, alpha 0.02, row scales fp16 of
                  U(0.5, 1.5), x bf16 [2048, 8192].
+
+Variants of the Route B layer (their own seeds):
+
+  routeb_encode   fp32 weights for the encoder (seed 5).
+  routeb_blocks   codes as routeb_gemv, one ladder per block of 32 rows
+                  (each drawn as routeb_gemv's), alpha 0.02 (seed 6).
+  routeb_alphabet codes over an alphabet of 60 distinct codes drawn without
+                  replacement, letter j (j = 1..60) taken with probability
+                  proportional to 1/j: about 75 % of the weights use the 18
+                  commonest codes and 94 % the 45 commonest, near the code
+                  histogram the Route B page reports (section 8.1); ladder
+                  and alpha as routeb_gemv (seed 7).
 """
 
 import numpy as np
@@ -97,3 +109,24 @@ def routeb_prefill(seed=4, N=8192, K=8192, M=2048):
     x = _x(rng, M, K)
     return {"codes": codes, "ladder": ladder, "alpha": np.float32(0.02),
             "row_scale": rho, "x": x}
+
+
+def routeb_blocks(seed=6, N=8192, K=8192, M=1, table_rows=32):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 243, size=(N, K), dtype=np.uint8)
+    nb = -(-N // table_rows)
+    ladders = np.stack([_ladder(rng) for _ in range(nb)]) if nb else np.zeros((0, 5), np.float32)
+    x = _x(rng, M, K)
+    return {"codes": codes, "ladders": ladders, "table_rows": table_rows,
+            "alpha": np.float32(0.02), "x": x}
+
+
+def routeb_alphabet(seed=7, N=8192, K=8192, M=1, n_codes=60):
+    rng = np.random.default_rng(seed)
+    alphabet = rng.choice(243, size=n_codes, replace=False).astype(np.uint8)
+    p = 1.0 / np.arange(1, n_codes + 1)
+    p /= p.sum()
+    codes = alphabet[rng.choice(n_codes, size=(N, K), p=p)]
+    ladder = _ladder(rng)
+    x = _x(rng, M, K)
+    return {"codes": codes, "ladder": ladder, "alpha": np.float32(0.02), "x": x}
