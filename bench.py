@@ -57,9 +57,9 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="warm-up continues untimed until this many seconds of work have run")
     ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads)")
-    ap.add_argument("--extras", default="routeb,ternary,moe,encode,prefill",
+    ap.add_argument("--extras", default="routeb,ternary,moe,encode,prefill,blocks,alphabet",
                     help="comma list of extra workloads to time "
-                         "(routeb, ternary, moe, encode, prefill)")
+                         "(routeb, ternary, moe, encode, prefill, blocks, alphabet)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -436,12 +436,71 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         fn = lambda: dmm.rb_matmul(x, cd, table, float(d["alpha"]), y, rho)
         sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
         flops = 2.0 * 2048 * 8192 * 8192
-        res["routeb_prefill_M2048"] = {
-            "us_per_launch": round(sec * 1e6, 2),
-            "tflops": round(flops / sec / 1e12, 2),
-            "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        }
+        res["routeb_prefill_M2048"] = _prefill_rec(sec, flops)
+
+    if "blocks" in sel:
+        progress("extra: routeb_blocks (one code book per 32 rows)")
+        d = workloads.routeb_blocks(M=2048)
+        tables = to_dev(np.stack([dmm.rb_table(a) for a in d["ladders"]]))
+        c0 = to_dev(d["codes"])
+        bufs = [c0] + [c0.clone() for _ in range(7)]
+        x1 = to_dev(bits16(d["x"][:1]))
+        ys = [torch.empty((1, 8192), dtype=torch.bfloat16, device=dev) for _ in range(8)]
+        fn = lambda: [dmm.rb_matmul_blocks(x1, bufs[i], tables, 32, float(d["alpha"]), ys[i])
+                      for i in range(8)]
+        sec = _timed_launches(torch, fn, 8, use_graph)
+        b = 8192 * 8192 + 256 * 972 + 8192 * 4
+        res["routeb_blocks32_gemv_M1"] = _rec(b, sec, 1, 2 * 8192 * 8192)
+        del bufs, ys
+        x = to_dev(bits16(d["x"]))
+        y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=dev)
+        fn = lambda: dmm.rb_matmul_blocks(x, c0, tables, 32, float(d["alpha"]), y)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        res["routeb_blocks32_prefill_M2048"] = _prefill_rec(sec, 2.0 * 2048 * 8192 * 8192)
+        del x, y, c0
+
+    if "alphabet" in sel:
+        progress("extra: routeb_alphabet (7-bit indices)")
+        d = workloads.routeb_alphabet(M=2048)
+        table = to_dev(dmm.rb_table(d["ladder"]))
+        codes = to_dev(d["codes"])
+        L = dmm.rb7_row_bytes(8192)
+        used = torch.empty(128, dtype=torch.uint8, device=dev)
+        n_used = torch.empty(1, dtype=torch.int32, device=dev)
+        c7 = torch.empty((8192, L), dtype=torch.uint8, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        fn = lambda: dmm.rb_truncate(codes, used, n_used, c7, st)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        assert int(st.item()) == 0 and int(n_used.item()) == 60
+        res["routeb_truncate"] = {"us_per_call": round(sec * 1e6, 2),
+                                  "codes_per_s": round(8192 * 8192 / sec, 1)}
+        del codes
+        bufs = [c7] + [c7.clone() for _ in range(7)]
+        x1 = to_dev(bits16(d["x"][:1]))
+        ys = [torch.empty((1, 8192), dtype=torch.bfloat16, device=dev) for _ in range(8)]
+        fn = lambda: [dmm.rb_matmul7(x1, bufs[i], 8192, used, table, 0, float(d["alpha"]), ys[i])
+                      for i in range(8)]
+        sec = _timed_launches(torch, fn, 8, use_graph)
+        b = 8192 * L + 128 + 972 + 8192 * 4
+        rec = _rec(b, sec, 1, 2 * 8192 * 8192)
+        rec["codes_used"] = 60
+        res["routeb7_gemv_M1"] = rec
+        del bufs, ys
+        x = to_dev(bits16(d["x"]))
+        y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=dev)
+        fn = lambda: dmm.rb_matmul7(x, c7, 8192, used, table, 0, float(d["alpha"]), y)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        res["routeb7_prefill_M2048"] = _prefill_rec(sec, 2.0 * 2048 * 8192 * 8192)
+        del x, y, c7
     return res
+
+
+def _prefill_rec(sec, flops):
+    return {
+        "us_per_launch": round(sec * 1e6, 2),
+        "tflops": round(flops / sec / 1e12, 2),
+        "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+    }
 
 
 def _rec(bytes_launch, sec, M, flops):

@@ -25,9 +25,11 @@ TQ_BF16 = 1
 TQ_DATA_RANGE = 1
 TQ_DATA_CODE = 2
 TQ_DATA_PADDING = 4
+TQ_DATA_ALPHABET = 8
 
 EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
-           "rb_matmul", "rb_matmul_rho_block", "tq_status_string")
+           "rb_matmul", "rb_matmul_rho_block", "rb_matmul_blocks", "rb_truncate",
+           "rb_matmul7", "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -51,10 +53,14 @@ _lib.rb_encode.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, _i32, _p, _p, _p,
 _lib.rb_matmul.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _p, _p, _i32, _p]
 _lib.rb_matmul_rho_block.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float, _p, _i32, _p,
                                      _p, _i32, _p]
+_lib.rb_matmul_blocks.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i32, ctypes.c_float, _p, _i32,
+                                  _p, _p, _i32, _p]
+_lib.rb_truncate.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _p]
+_lib.rb_matmul7.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p, _i32, ctypes.c_float, _p, _i32,
+                            _p, _p, _i32, _p]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
-for _name in ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
-              "rb_matmul", "rb_matmul_rho_block"):
+for _name in EXPORTS[:-1]:
     getattr(_lib, _name).restype = _i32
 
 
@@ -256,6 +262,77 @@ def rb_matmul(x, codes, table, alpha, y, row_scale=None, bias=None, rho_rows=1):
                                       _ptr(row_scale), int(rho_rows), _ptr(bias), _ptr(y),
                                       _ydtype(y), _stream(dev))
     _raise(rc, "rb_matmul")
+
+
+def _tables(tables, N, table_rows, dev):
+    nb = -(-N // int(table_rows)) if table_rows > 0 else 1
+    _need(tables, "tables", _F32, nb * 243, dev)
+
+
+def rb_matmul_blocks(x, codes, tables, table_rows, alpha, y, row_scale=None, bias=None,
+                     rho_rows=1):
+    """rb_matmul with code book tables[n // table_rows] for row n (fp32
+    [ceil(N / table_rows), 243]; table_rows a multiple of 32, or 0 for one
+    book)."""
+    dev = x.device
+    M, K = x.shape
+    N = codes.shape[0]
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes, "codes", _U8, N * K, dev)
+    _tables(tables, N, table_rows, dev)
+    if row_scale is not None:
+        _need(row_scale, "row_scale", _H16, -(-N // int(rho_rows)) if rho_rows > 0 else N, dev)
+    if bias is not None:
+        _need(bias, "bias", _F32, N, dev)
+    _need(y, "y", (y.dtype,), M * N, dev)
+    rc = _lib.rb_matmul_blocks(_ptr(x), M, K, _ptr(codes), N, _ptr(tables), int(table_rows),
+                               float(alpha), _ptr(row_scale), int(rho_rows), _ptr(bias), _ptr(y),
+                               _ydtype(y), _stream(dev))
+    _raise(rc, "rb_matmul_blocks")
+
+
+def rb7_row_bytes(K):
+    """Bytes per row of 7-bit indices."""
+    return -(-7 * int(K) // 8)
+
+
+def rb_truncate(codes, used, n_used, codes7, status=None):
+    """uint8 codes [N, K] -> used uint8 [128] (increasing used codes, padded
+    with 121), n_used int32 [1] and codes7 uint8 [N, ceil(7 K / 8)]."""
+    dev = codes.device
+    N, K = codes.shape
+    _need(codes, "codes", _U8, N * K, dev)
+    _need(used, "used", _U8, 128, dev)
+    _need(n_used, "n_used", _I32, 1, dev)
+    _need(codes7, "codes7", _U8, N * rb7_row_bytes(K), dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(status, "status", _I32, 1, dev)
+    rc = _lib.rb_truncate(_ptr(codes), N, K, _ptr(used), _ptr(n_used), _ptr(codes7),
+                          _ptr(status), _stream(dev))
+    _raise(rc, "rb_truncate")
+    return status
+
+
+def rb_matmul7(x, codes7, N, used, tables, table_rows, alpha, y, row_scale=None, bias=None,
+               rho_rows=1):
+    """Route B matmul over 7-bit indices codes7 [N, ceil(7 K / 8)]: weight
+    (n, k) is tables[n // table_rows][used[index]] (table_rows 0: one book)."""
+    dev = x.device
+    M, K = x.shape
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes7, "codes7", _U8, N * rb7_row_bytes(K), dev)
+    _need(used, "used", _U8, 128, dev)
+    _tables(tables, N, table_rows, dev)
+    if row_scale is not None:
+        _need(row_scale, "row_scale", _H16, -(-N // int(rho_rows)) if rho_rows > 0 else N, dev)
+    if bias is not None:
+        _need(bias, "bias", _F32, N, dev)
+    _need(y, "y", (y.dtype,), M * N, dev)
+    rc = _lib.rb_matmul7(_ptr(x), M, K, _ptr(codes7), N, _ptr(used), _ptr(tables),
+                         int(table_rows), float(alpha), _ptr(row_scale), int(rho_rows),
+                         _ptr(bias), _ptr(y), _ydtype(y), _stream(dev))
+    _raise(rc, "rb_matmul7")
 
 
 def raw():

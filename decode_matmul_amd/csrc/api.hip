@@ -198,13 +198,17 @@ int rb_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int
                                stream);
 }
 
-int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
-                        const float* table, float alpha, const uint16_t* row_scale,
-                        int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
-                        void* stream) {
+// Every Route B matmul: code bytes (used == NULL) or 7-bit indices, one code
+// book (table_rows == 0) or one per block of table_rows rows.
+static int rb_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
+                            const uint8_t* used, int64_t N, const float* table,
+                            int32_t table_rows, float alpha, const uint16_t* row_scale,
+                            int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
+                            void* stream) {
     if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
         return TQ_ERR_SHAPE;
-    if (rho_rows < 1) return TQ_ERR_SHAPE;
+    if (rho_rows < 1 || table_rows < 0) return TQ_ERR_SHAPE;
+    if (table_rows % 32 != 0) return TQ_ERR_UNSUPPORTED;
     if (y_dtype != TQ_F32 && y_dtype != TQ_BF16) return TQ_ERR_DTYPE;
     if (M == 0 || N == 0) return TQ_OK;
     if (!table || !y || (K > 0 && (!x || !codes))) return TQ_ERR_NULL;
@@ -217,7 +221,9 @@ int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
     a.K = K;
     a.N = N;
     a.codes = codes;
+    a.used = used;
     a.table = table;
+    a.table_rows = table_rows;
     a.alpha = alpha;
     a.row_scale = row_scale;
     a.rho_rows = rho_rows;
@@ -227,10 +233,46 @@ int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
     hipStream_t s = (hipStream_t)stream;
     if (M <= 16) {
         if ((N + 15) / 16 >= kMaxDim) return TQ_ERR_SHAPE;
-        return hip_status(dmm::launch_rb_gemv(a, s));
+        return hip_status(used ? dmm::launch_rb7_gemv(a, s) : dmm::launch_rb_gemv(a, s));
     }
     if ((M + 255) / 256 >= 65536) return TQ_ERR_SHAPE;
     return hip_status(dmm::launch_rb_prefill(a, s));
+}
+
+int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                        const float* table, float alpha, const uint16_t* row_scale,
+                        int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
+                        void* stream) {
+    return rb_matmul_common(x, M, K, codes, nullptr, N, table, 0, alpha, row_scale, rho_rows,
+                            bias, y, y_dtype, stream);
+}
+
+int rb_matmul_blocks(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                     const float* tables, int32_t table_rows, float alpha,
+                     const uint16_t* row_scale, int32_t rho_rows, const float* bias, void* y,
+                     int32_t y_dtype, void* stream) {
+    return rb_matmul_common(x, M, K, codes, nullptr, N, tables, table_rows, alpha, row_scale,
+                            rho_rows, bias, y, y_dtype, stream);
+}
+
+int rb_truncate(const uint8_t* codes, int64_t N, int64_t K, uint8_t* used_out,
+                int32_t* n_used_out, uint8_t* codes7, int32_t* d_status, void* stream) {
+    if (!used_out || !n_used_out || !d_status) return TQ_ERR_NULL;
+    if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return TQ_ERR_SHAPE;
+    if (N > 0 && K > 0 && (!codes || !codes7)) return TQ_ERR_NULL;
+    if (!aligned(used_out, 4) || !aligned(n_used_out, 4) || !aligned(d_status, 4))
+        return TQ_ERR_ALIGN;
+    return hip_status(dmm::launch_rb_truncate(codes, N, K, used_out, n_used_out, codes7, d_status,
+                                              (hipStream_t)stream));
+}
+
+int rb_matmul7(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes7, int64_t N,
+               const uint8_t* used, const float* tables, int32_t table_rows, float alpha,
+               const uint16_t* row_scale, int32_t rho_rows, const float* bias, void* y,
+               int32_t y_dtype, void* stream) {
+    if (!used) return TQ_ERR_NULL;
+    return rb_matmul_common(x, M, K, codes7, used, N, tables, table_rows, alpha, row_scale,
+                            rho_rows, bias, y, y_dtype, stream);
 }
 
 }  // extern "C"

@@ -12,6 +12,7 @@ namespace dmm {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 // 16-byte vectors loaded from 4-byte aligned addresses.
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
@@ -61,6 +62,16 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// A code-book entry as two bf16 terms packed in one dword: hi = bf16(v) in
+// the low half, lo = bf16(v - hi) in the high half (v - hi is exact, and
+// |v - hi - lo| <= 2^-17 |v|).
+__device__ __forceinline__ uint32_t split_bf16_pair(float v) {
+    const uint16_t hi = f32_to_bf16_rne(v);
+    const float r = v - bf16_bits_to_f32(hi);
+    const uint16_t lo = f32_to_bf16_rne(r);
+    return (uint32_t)hi | ((uint32_t)lo << 16);
 }
 
 // Bytes [sh, sh+4) of the 8-byte little-endian value {hi:lo}, sh in 0..3.
@@ -150,8 +161,10 @@ int tq_max_grouped_pairs();  // largest M * top_k of a grouped call
 struct RbMatmulArgs {
     const uint16_t* x;
     int64_t M, K, N;
-    const uint8_t* codes;
-    const float* table;
+    const uint8_t* codes;   // one byte per weight, or 7-bit indices when `used` is set
+    const uint8_t* used;    // 7-bit form: index -> code, [128]; NULL for code bytes
+    const float* table;     // [243], or [ceil(N / table_rows)][243]
+    int64_t table_rows;     // 0: one code book; else rows per code book (a multiple of 32)
     float alpha;
     const uint16_t* row_scale;
     int64_t rho_rows;       // rows sharing one row_scale entry (>= 1)
@@ -160,8 +173,21 @@ struct RbMatmulArgs {
     int y_dtype;
 };
 
+// Bytes of one row of 7-bit indices.
+inline int64_t rb7_row_bytes(int64_t K) { return (7 * K + 7) / 8; }
+
+// Code book of the rows starting at row0 (table_rows is a multiple of 32, so
+// a 16- or 32-row block of rows shares one).
+__host__ __device__ inline const float* rb_table_of(const float* table, int64_t table_rows,
+                                                    int64_t row0) {
+    return table + (table_rows > 0 ? row0 / table_rows : 0) * 243;
+}
+
 hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s);
+hipError_t launch_rb7_gemv(const RbMatmulArgs& a, hipStream_t s);
 hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s);
+hipError_t launch_rb_truncate(const uint8_t* codes, int64_t N, int64_t K, uint8_t* used,
+                              int32_t* n_used, uint8_t* codes7, int32_t* status, hipStream_t s);
 hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
                             int64_t rho_rows, uint8_t* codes, float* alpha, uint16_t* row_scale,
                             int32_t* status, hipStream_t s);

@@ -4,7 +4,9 @@
 // B), section 3.2 (codes index a 243-entry code book), section 3.3 (per-row
 // scale rho_n) and section 4.2 (the code book sits in on-chip memory, every
 // code byte is dereferenced through it inside a K-sliced GEMM, rho_n is
-// applied to the accumulator before the bias).
+// applied to the accumulator before the bias).  With per-block code books
+// (section 8.3: one ladder per block of 32 rows) T is the book of the row's
+// block; a workgroup's rows lie in one block, so it stages that one.
 //
 // Mapping onto gfx950:
 //  * General path: the workgroup (16 waves, one per CU: the replicated table
@@ -48,6 +50,7 @@ struct Params {
     int64_t M, K, N;
     const uint8_t* codes;
     const float* table;
+    int64_t table_rows;                      // 0: one code book; else rows per code book
     float alpha;
     const uint16_t* row_scale;
     int64_t rho_rows;                        // rows sharing one row_scale entry
@@ -57,13 +60,6 @@ struct Params {
     int64_t steps;                           // ceil(K / 64)
     int64_t full_steps;                      // steps entirely inside K
 };
-
-__device__ __forceinline__ uint32_t split_entry(float v) {
-    uint16_t hi = f32_to_bf16_rne(v);
-    float r = v - bf16_bits_to_f32(hi);      // exact
-    uint16_t lo = f32_to_bf16_rne(r);
-    return (uint32_t)hi | ((uint32_t)lo << 16);
-}
 
 // Raw words holding the 16 code bytes of row `row` at column k (k + 16 <= K).
 // ALIGNED: row + k is 4-byte aligned, the four words are the bytes.
@@ -145,7 +141,8 @@ rb_gemv_kernel(Params p) {
 
     {   // entry b, copies 16 (tid & 3) .. + 15: one global read per thread
         const int b = tid >> 2;
-        const uint32_t e = split_entry(b < 243 ? p.table[b] : 0.f);
+        const float* table = rb_table_of(p.table, p.table_rows, (int64_t)blockIdx.x * 16 * kRB);
+        const uint32_t e = split_bf16_pair(b < 243 ? table[b] : 0.f);
         const u32x4 q = {e, e, e, e};
         unsigned char* base = lut + b * 256 + (tid & 3) * 64;
 #pragma unroll
@@ -353,13 +350,13 @@ rb_gemv_tiled_kernel(Params p) {
     // the code-book read goes first so that waiting for it leaves the tile
     // loads in flight (memory counters complete in order)
     const int lb = tid >> 1;
-    const float tv = p.table[lb < 243 ? lb : 0];
+    const float tv = rb_table_of(p.table, p.table_rows, row0)[lb < 243 ? lb : 0];
     Stage s0, s1;
     fetch(0, s0);
     fetch(1, s1);
 
     {   // entry b, copies 8 (tid & 1) .. + 7; entries 243..255 read zero
-        const uint32_t e = split_entry(lb < 243 ? tv : 0.f);
+        const uint32_t e = split_bf16_pair(lb < 243 ? tv : 0.f);
         const u32x4 q = {e, e, e, e};
         unsigned char* base = lut + lb * 4 * kTCopies + (tid & 1) * 2 * kTCopies;
         *(u32x4*)base = q;
@@ -448,6 +445,7 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
     p.N = a.N;
     p.codes = a.codes;
     p.table = a.table;
+    p.table_rows = a.table_rows;
     p.alpha = a.alpha;
     p.row_scale = a.row_scale;
     p.rho_rows = a.rho_rows;

@@ -32,12 +32,26 @@
 //    slice s run from registers, the next K-step's fragments are read and
 //    slice s + 2 (loaded from global memory an iteration earlier) is decoded
 //    into the buffer slice s has just vacated.  One barrier per slice.
-//  * The code book sits in LDS in 32 copies: entry b of copy c at byte
-//    (b << 8) | (c << 2) holds the fp16 value, and 128 bytes further the
-//    (hi, lo) bf16 pair.  One v_perm of the code word and the lane offset
-//    forms the address; the 32 lanes of a phase hit distinct banks.
+//  * The code book sits in LDS in 8 slots of 4 copies: slot h serves tile
+//    rows 32 h .. 32 h + 31 (with one book per block of 32 rows, section
+//    8.3, each slot holds its block's book; with one book, all eight hold
+//    it).  Entry b of slot h, copy c, at byte (b << 8) | (h << 4) | (c << 2)
+//    holds the fp16 value, and 128 bytes further the (hi, lo) bf16 pair; a
+//    slot's book has its own power-of-two scale sigma_h.  One v_perm of the
+//    code word and the lane offset forms the address.
+//  * A thread decodes 16 codes of tile row 32 (q % 8) + q / 8 (q = thread /
+//    2), so the lanes of a phase spread over the 8 slots and, with the copy
+//    index, over distinct banks.  The decoded row goes to LDS row
+//    32 h + (j ^ s_h) (row j of slot h, s_h = 0, 1, 4, 5, 8, 9, 12, 13): the
+//    16-byte stores of a phase then cover distinct banks, and the fragment
+//    reads (32 consecutive rows of one slot) stay conflict-free.
 //  * Tile rows are 80 bytes apart, so the 8 lanes of a 16-byte column read
 //    cover all 32 banks.
+//  * 7-bit indices (section 8.1): a K-slice of a row is 28 bytes; the two
+//    threads of a row load 16 bytes at byte 0 and 12, funnel-shift the
+//    second by 16 bits, and index i is then bit 7 i of the four dwords; one
+//    shift and one and-or give its address in the book, whose entry j is
+//    T[used[j]].
 #include "common.h"
 
 namespace dmm {
@@ -51,8 +65,12 @@ constexpr int MT = 4, NT = 2;                  // 32x32 MFMA tiles per wave alon
 constexpr int kPitch = 2 * BK + 16;            // bytes per LDS tile row
 constexpr int kTileBytes = BM * kPitch;        // one operand tile (BM == BN)
 constexpr int kLutBytes = 256 * 256;
+constexpr int kSlots = 8;                      // code-book slots (32 tile rows each)
 constexpr int kMapSlices = 1536;                // slices tracked one by one (K <= 49152)
-constexpr int kSmemBytes = kLutBytes + 4 * kTileBytes + 96 + 8 * (kMapSlices + 1);
+constexpr int kWords = 64 + 4 * 4 * kThreads / 64 + 32;   // flags, maxima, slot exponents
+constexpr int kSmemBytes = kLutBytes + 4 * kTileBytes + kWords + 8 * (kMapSlices + 1);
+static_assert(kSlots * 32 == BN, "one slot per 32 tile rows");
+static_assert(kSmemBytes <= 160 * 1024, "fits the LDS of a CU");
 static_assert(kThreads / 64 <= 8, "one flag byte per wave");
 static_assert(kMapSlices * 2 <= 2 * kTileBytes, "the slice list fits LDS buffer 1");
 static_assert(BM == BN, "square tiles share one pitch");
@@ -63,8 +81,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 struct Params {
     const uint16_t* x;
     int64_t M, K, N;
-    const uint8_t* codes;
+    const uint8_t* codes;                    // code bytes, or 7-bit rows
+    int64_t row_bytes;                       // bytes per row of codes
+    const uint8_t* used;                     // 7-bit form: index -> code [128]
     const float* table;
+    int64_t table_rows;                      // 0: one code book; else rows per book
     float alpha;
     const uint16_t* row_scale;
     int64_t rho_rows;                        // rows sharing one row_scale entry
@@ -73,6 +94,28 @@ struct Params {
     int y_dtype;
 };
 
+// Row j of slot h sits in LDS row 32 h + (j ^ row_swizzle(h)).
+__device__ __forceinline__ int row_swizzle(int h) { return (h & 1) | ((h & 6) << 1); }
+
+// Index k of a 7-bit row (byte-granular reads).
+__device__ __forceinline__ uint32_t load_index7(const uint8_t* row, int64_t row_bytes, int64_t k) {
+    const int64_t bit = 7 * k;
+    const int64_t b = bit >> 3;
+    uint32_t v = row[b];
+    if (b + 1 < row_bytes) v |= (uint32_t)row[b + 1] << 8;
+    return (v >> (bit & 7)) & 0x7fu;
+}
+
+// Book address (index << 8) | off of index i (constant after unrolling) of
+// 16 indices held at bits 7 i of F[0..3].
+__device__ __forceinline__ uint32_t index7_addr(const uint32_t* F, int i, uint32_t off) {
+    const int bit = 7 * i, d = bit >> 5, o = bit & 31;
+    uint32_t v;
+    if (o + 7 <= 32) v = o >= 8 ? F[d] >> (o - 8) : F[d] << (8 - o);
+    else v = __builtin_amdgcn_alignbit(F[d + 1], F[d], (uint32_t)(o - 8));
+    return (v & 0x7f00u) | off;
+}
+
 // Per-thread loads of one K-slice: 2 chunks of 8 activations, 1 chunk of 16 codes.
 constexpr int XCH = BM * BK / 8 / kThreads, CCH = BN * BK / 16 / kThreads;
 struct Slice {
@@ -80,7 +123,8 @@ struct Slice {
     u32x4 cd[CCH];
 };
 
-template <bool AL>
+// AL: 16-byte aligned activations and codes, K % 32 == 0.  C7: 7-bit indices.
+template <bool AL, bool C7>
 __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     // one LDS block: the code book at address 0 (so a v_perm result is its
     // own address), two buffers of (activation, weight) tiles, a few words
@@ -91,10 +135,11 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     unsigned char* const words = smem + kLutBytes + 4 * kTileBytes;
     int& table_bad = *(int*)(words);
     int& redo_n = *(int*)(words + 8);
-    float* const red_max = (float*)(words + 64);
+    float* const red_max = (float*)(words + 64);                 // [wave][4]
+    int* const slot_exp = (int*)(words + kWords - 32);           // [kSlots]
     // one flag word per slice s < kMapSlices, one byte per wave (written by
     // the whole wave, so no atomics); word kMapSlices collects later slices
-    uint64_t* const bad_map = (uint64_t*)(words + 96);
+    uint64_t* const bad_map = (uint64_t*)(words + kWords);
     uint16_t* const redo = (uint16_t*)tiles2[2];        // list of flagged slices (buffer 1, idle then)
 
     const int tid = threadIdx.x;
@@ -102,52 +147,76 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     const int wave = readfirstlane(tid >> 6);
     const int wm = wave / kWN, wn = wave % kWN;
 
-    // ---- code book scale: sigma = 2^j with max |sigma T| in [2^14, 2^15)
-    float tv = 0.f;
-    if ((tid & 255) < 243) tv = p.table[tid & 255];
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+
+    // ---- code books: thread tid fills entry b = tid % 256 of slots
+    // tid / 256 + 2 i (i < 4).  Slot h scales its book by sigma_h = 2^j_h
+    // with max |sigma_h T| in [2^14, 2^15).
+    const int eb = tid & 255;
+    float tv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = (tid >> 8) + 2 * i;
+        const float* table = rb_table_of(p.table, p.table_rows, min(n0 + 32 * h, p.N - 1));
+        if constexpr (C7) {
+            const uint32_t c = p.used[eb & 127];
+            const float v = table[c < 243 ? c : 0];
+            tv[i] = (eb < 128 && c < 243) ? v : 0.f;
+        } else {
+            const float v = table[eb < 243 ? eb : 0];
+            tv[i] = eb < 243 ? v : 0.f;
+        }
+    }
     {
-        float a = fabsf(tv);
-        for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-        if (lane == 0) red_max[wave] = a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float a = fabsf(tv[i]);
+            for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+            if (lane == 0) red_max[wave * 4 + i] = a;
+        }
         if (tid == 0) { table_bad = 0; redo_n = 0; }
         for (int i = tid; i <= kMapSlices; i += kThreads) bad_map[i] = 0ull;
     }
     __syncthreads();
-    float tmax = red_max[0];
+    if (tid < kSlots) {                 // slot tid: waves 4 (tid & 1) .. + 3, column tid / 2
+        float tmax = 0.f;
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) tmax = fmaxf(tmax, red_max[w]);
-    int e2 = 0;
-    if (tmax > 0.f && tmax <= 3.0e38f) (void)frexpf(tmax, &e2);     // tmax < 2^e2
-    const int j = min(max(15 - e2, -120), 120);
-    const float sigma = ldexpf(1.f, j), inv_sigma = ldexpf(1.f, -j);
-    {
-        // entry tid (zero for the 13 padding codes): fp16 of sigma T and the bf16 hi/lo pair
-        const float s = tv * sigma;                                   // exact power-of-two scaling
-        const _Float16 h = (_Float16)s;                               // nearest-even
-        const uint32_t hb = __builtin_bit_cast(uint16_t, h);
+        for (int w = 0; w < 4; ++w) tmax = fmaxf(tmax, red_max[(4 * (tid & 1) + w) * 4 + (tid >> 1)]);
+        int e2 = 0;
+        if (tmax > 0.f && tmax <= 3.0e38f) (void)frexpf(tmax, &e2);     // tmax < 2^e2
+        slot_exp[tid] = min(max(15 - e2, -120), 120);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // entry eb of slot h (zero for padding codes): fp16 of sigma_h T and
+        // the bf16 hi/lo pair, in the slot's 4 copies
+        const int h = (tid >> 8) + 2 * i;
+        const float s = tv[i] * ldexpf(1.f, slot_exp[h]);              // exact power-of-two scaling
+        const _Float16 hf = (_Float16)s;                                // nearest-even
+        const uint32_t hb = __builtin_bit_cast(uint16_t, hf);
         const bool ok = (s == 0.f) || (fabsf(s) >= 0x1p-14f && fabsf(s) <= 65504.f);
-        if ((tid & 255) < 243 && !ok) table_bad = 1;
+        if (!ok) table_bad = 1;
         const uint16_t hi = f32_to_bf16_rne(s);
         const uint16_t lo = f32_to_bf16_rne(s - bf16_bits_to_f32(hi));
         const uint32_t fb = (uint32_t)hi | ((uint32_t)lo << 16);
-        // entry tid & 255, copies 16 (tid >> 8) .. +15
-        const int b = tid & 255;
-#pragma unroll 4
-        for (int c = 16 * (tid >> 8); c < 16 * (tid >> 8) + 16; ++c) {
-            *(uint32_t*)(lut + ((b << 8) | (c << 2))) = hb;
-            *(uint32_t*)(lut + ((b << 8) | 128 | (c << 2))) = fb;
-        }
+        unsigned char* e = lut + ((eb << 8) | (h << 4));
+        *(u32x4*)e = u32x4{hb, hb, hb, hb};
+        *(u32x4*)(e + 128) = u32x4{fb, fb, fb, fb};
     }
 
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int nslices = (int)((p.K + BK - 1) / BK);
-    const uint32_t cofs = (uint32_t)(lane & 31) << 2;
 
     // this thread's chunks: activations (rows xr + 128 i, 8 values at column
-    // 8 xc), codes (row cr, 16 bytes at column 16 cc)
+    // 8 xc), codes (tile row cr = 32 ch + cj, 16 codes at column 16 cc),
+    // decoded through slot ch, copy 2 (cj & 1) + cc, into LDS row crs
     const int xc = tid & 3, xr = tid >> 2;
-    const int cc = tid & 1, cr = tid >> 1;
+    const int cc = tid & 1, cq = tid >> 1;
+    const int ch = cq & 7, cj = cq >> 3;
+    const int cr = 32 * ch + cj;
+    const int crs = 32 * ch + (cj ^ row_swizzle(ch));
+    const uint32_t cofs = (uint32_t)((ch << 4) | ((((cj & 1) << 1) | cc) << 2));
     static_assert(XCH == 2 && CCH == 1, "chunk mapping");
 
     auto gload = [&](int s, Slice& S) {
@@ -158,11 +227,11 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
                 const int64_t m = min(m0 + xr + 128 * i, p.M - 1);
                 S.xa[i] = *(const u32x4*)(p.x + m * p.K + k0 + 8 * xc);
             }
-#pragma unroll
-            for (int i = 0; i < CCH; ++i) {
-                const int64_t n = min(n0 + cr + 256 * i, p.N - 1);
-                S.cd[i] = *(const u32x4*)(p.codes + n * p.K + k0 + 16 * cc);
-            }
+            const int64_t n = min(n0 + cr, p.N - 1);
+            if constexpr (C7)      // 28 bytes per slice: dwords 0..3 or 3..6
+                S.cd[0] = *(const u32x4a*)(p.codes + n * p.row_bytes + (k0 / BK) * 28 + 12 * cc);
+            else
+                S.cd[0] = *(const u32x4*)(p.codes + n * p.row_bytes + k0 + 16 * cc);
         } else {
             // element loads: activations past M or K are 0, codes past N or K
             // are 255 (a zero entry of the padded table)
@@ -180,20 +249,20 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
                     S.xa[i][w] = lo | (hi << 16);
                 }
             }
+            // (7-bit indices arrive one per byte, as code bytes do)
+            const int64_t n = n0 + cr;
+            const uint8_t* row = p.codes + (n < p.N ? n : 0) * p.row_bytes;
 #pragma unroll
-            for (int i = 0; i < CCH; ++i) {
-                const int64_t n = n0 + cr + 256 * i;
+            for (int w = 0; w < 4; ++w) {
+                uint32_t v = 0;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t v = 0;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const int64_t k = k0 + 16 * cc + 4 * w + b;
-                        const uint32_t c = (n < p.N && k < p.K) ? p.codes[n * p.K + k] : 0xffu;
-                        v |= c << (8 * b);
-                    }
-                    S.cd[i][w] = v;
+                for (int b = 0; b < 4; ++b) {
+                    const int64_t k = k0 + 16 * cc + 4 * w + b;
+                    uint32_t c = 0xffu;
+                    if (n < p.N && k < p.K) c = C7 ? load_index7(row, p.row_bytes, k) : row[k];
+                    v |= c << (8 * b);
                 }
+                S.cd[0][w] = v;
             }
         }
     };
@@ -202,26 +271,35 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     // (word at + 128, part 0 / 1)
     auto store_weights = [&](int buf, const Slice& S, uint32_t lut_off, uint32_t sel) {
         unsigned char* B = tiles2[2 * buf + 1];
-#pragma unroll
-        for (int i = 0; i < CCH; ++i) {
-            u32x4 o0, o1;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t d = S.cd[i][w];
-                uint32_t e[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    e[b] = *(const uint32_t*)(lut + lut_off +
-                                              perm_b32(d, cofs, 0x0c0c0400u + ((uint32_t)b << 8)));
-                const uint32_t p01 = perm_b32(e[1], e[0], sel);
-                const uint32_t p23 = perm_b32(e[3], e[2], sel);
-                if (w < 2) { o0[2 * w] = p01; o0[2 * w + 1] = p23; }
-                else { o1[2 * w - 4] = p01; o1[2 * w - 3] = p23; }
-            }
-            unsigned char* dst = B + (cr + 256 * i) * kPitch + 32 * cc;
-            *(u32x4*)dst = o0;
-            *(u32x4*)(dst + 16) = o1;
+        uint32_t F[4];
+        if constexpr (C7 && AL) {
+            // the second thread of a row loaded from dword 3: drop 16 bits so
+            // that index i of either thread sits at bit 7 i
+            const uint32_t sh = 16u * (uint32_t)cc;
+            F[0] = __builtin_amdgcn_alignbit(S.cd[0][1], S.cd[0][0], sh);
+            F[1] = __builtin_amdgcn_alignbit(S.cd[0][2], S.cd[0][1], sh);
+            F[2] = __builtin_amdgcn_alignbit(S.cd[0][3], S.cd[0][2], sh);
+            F[3] = S.cd[0][3] >> sh;
         }
+        u32x4 o0, o1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t e[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                uint32_t a;
+                if constexpr (C7 && AL) a = index7_addr(F, 4 * w + b, cofs | lut_off);
+                else a = perm_b32(S.cd[0][w], cofs | lut_off, 0x0c0c0400u + ((uint32_t)b << 8));
+                e[b] = *(const uint32_t*)(lut + a);
+            }
+            const uint32_t p01 = perm_b32(e[1], e[0], sel);
+            const uint32_t p23 = perm_b32(e[3], e[2], sel);
+            if (w < 2) { o0[2 * w] = p01; o0[2 * w + 1] = p23; }
+            else { o1[2 * w - 4] = p01; o1[2 * w - 3] = p23; }
+        }
+        unsigned char* dst = B + crs * kPitch + 32 * cc;
+        *(u32x4*)dst = o0;
+        *(u32x4*)(dst + 16) = o1;
     };
 
     // fp16 activations and weights of a slice into buffer buf.  A chunk of 8
@@ -285,20 +363,28 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
         }
 
     // A fragment: lane l holds A[l % 32][8 (l / 32) .. +7]; B alike with the
-    // rows of the weight tile.  One K-step (16) of a slice per Frag.
+    // rows of the weight tile (tile rows 32 h + l % 32 of slot h = NT wn + jn,
+    // at their swizzled LDS rows).  One K-step (16) of a slice per Frag.
     const int frow = lane & 31;
     const int fk = 16 * (lane >> 5);
+    static_assert(NT * 32 * kWN == BN, "a wave's B tiles are whole slots");
+    int brow[NT];
+#pragma unroll
+    for (int jn = 0; jn < NT; ++jn) {
+        const int h = wn * NT + jn;
+        brow[jn] = (32 * h + (frow ^ row_swizzle(h))) * kPitch;
+    }
     struct Frag {
         u32x4 a[MT];
         u32x4 b[NT];
     };
     auto load_frag = [&](int abuf, int bbuf, int ks, Frag& F) {
         const unsigned char* A = tiles2[2 * abuf] + (wm * 32 * MT + frow) * kPitch + fk + 32 * ks;
-        const unsigned char* B = tiles2[2 * bbuf + 1] + (wn * 32 * NT + frow) * kPitch + fk + 32 * ks;
+        const unsigned char* B = tiles2[2 * bbuf + 1] + fk + 32 * ks;
 #pragma unroll
         for (int i = 0; i < MT; ++i) F.a[i] = *(const u32x4*)(A + i * 32 * kPitch);
 #pragma unroll
-        for (int jn = 0; jn < NT; ++jn) F.b[jn] = *(const u32x4*)(B + jn * 32 * kPitch);
+        for (int jn = 0; jn < NT; ++jn) F.b[jn] = *(const u32x4*)(B + brow[jn]);
     };
     auto mfma_frag = [&](const Frag& F, bool f16) {
 #pragma unroll
@@ -397,6 +483,7 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     for (int jn = 0; jn < NT; ++jn) {
         const int64_t n = n0 + wn * 32 * NT + jn * 32 + (lane & 31);
         if (n >= p.N) continue;
+        const float inv_sigma = ldexpf(1.f, -slot_exp[wn * NT + jn]);
         const float rho = p.row_scale ? f16_bits_to_f32(p.row_scale[n / p.rho_rows]) : 1.f;
         const float bias = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
@@ -426,23 +513,30 @@ hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s) {
     p.K = a.K;
     p.N = a.N;
     p.codes = a.codes;
+    p.used = a.used;
+    p.row_bytes = a.used ? rb7_row_bytes(a.K) : a.K;
     p.table = a.table;
+    p.table_rows = a.table_rows;
     p.alpha = a.alpha;
     p.row_scale = a.row_scale;
     p.rho_rows = a.rho_rows;
     p.bias = a.bias;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
-    const bool aligned = (((uintptr_t)a.x & 15) == 0) && (((uintptr_t)a.codes & 15) == 0) &&
-                         (a.K % BK == 0);
+    // vector loads: 16-byte activation rows; code rows of 16 bytes a slice
+    // (bytes) or 28-byte slices on 4-byte boundaries (7-bit indices)
+    const bool aligned = (((uintptr_t)a.x & 15) == 0) && (a.K % BK == 0) &&
+                         (((uintptr_t)a.codes & (a.used ? 3 : 15)) == 0);
     const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
     if (gx == 0 || gy == 0) return hipSuccess;
-    if (aligned)
-        hipLaunchKernelGGL(rb_prefill_kernel<true>, dim3((unsigned)gx, (unsigned)gy),
-                           dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(rb_prefill_kernel<false>, dim3((unsigned)gx, (unsigned)gy),
-                           dim3(kThreads), 0, s, p);
+    const dim3 grid((unsigned)gx, (unsigned)gy), block(kThreads);
+    if (a.used) {
+        if (aligned) hipLaunchKernelGGL((rb_prefill_kernel<true, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((rb_prefill_kernel<false, true>), grid, block, 0, s, p);
+    } else {
+        if (aligned) hipLaunchKernelGGL((rb_prefill_kernel<true, false>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((rb_prefill_kernel<false, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -62,8 +62,10 @@ enum tq_status {
 /* Device-side data-error flags, OR-ed into *d_status. */
 enum tq_data_flag {
     TQ_DATA_RANGE = 1,       /* non-finite weight, or group scale overflows fp16 */
-    TQ_DATA_CODE = 2,        /* byte value 243..255 in a ternary package         */
-    TQ_DATA_PADDING = 4      /* a padding trit slot does not decode to zero      */
+    TQ_DATA_CODE = 2,        /* byte value 243..255 in a ternary package or as a
+                                Route B code                                     */
+    TQ_DATA_PADDING = 4,     /* a padding trit slot does not decode to zero      */
+    TQ_DATA_ALPHABET = 8     /* more than 128 distinct Route B codes (rb_truncate) */
 };
 
 /* Element types of outputs. */
@@ -265,6 +267,77 @@ int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         const float* table, float alpha, const uint16_t* row_scale,
                         int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
                         void* stream);
+
+/*
+ * rb_matmul_blocks -- Route B matmul with one code book per block of rows
+ * (Route B paper, section 8.3, adaptive alphabets: one ladder per group of 32
+ * rows instead of one per layer family):
+ *
+ *     y[m, n] = alpha * rho_{n / rho_rows} * sum_k x[m, k] * tables[n / table_rows][codes[n, k]]
+ *               (+ bias[n])
+ *
+ *  tables      device fp32 [ceil(N / table_rows)][243], 4-byte aligned; book
+ *              h serves rows h * table_rows .. (h + 1) * table_rows - 1 (e.g.
+ *              rb_table of block h's ladder).
+ *  table_rows  a positive multiple of 32, or 0 for one book of 243 entries
+ *              (TQ_ERR_UNSUPPORTED for other values, TQ_ERR_SHAPE if
+ *              negative).
+ *
+ * Every other argument, the kernels and the accuracy are those of
+ * rb_matmul_rho_block (which is this call with table_rows = 0).
+ */
+int rb_matmul_blocks(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                     const float* tables, int32_t table_rows, float alpha,
+                     const uint16_t* row_scale, int32_t rho_rows, const float* bias, void* y,
+                     int32_t y_dtype, void* stream);
+
+/*
+ * rb_truncate -- the 7-bit truncated alphabet (Route B paper, section 8.1: a
+ * layer that uses at most 128 of the 243 codes stores each weight in 7 bits,
+ * plus a table from the 7-bit index to the code).
+ *
+ *  codes       device uint8 [N, K] Route B code bytes, any alignment.
+ *  used_out    device uint8 [128], 4-byte aligned: the codes present, in
+ *              increasing order, then code 121 (the all-zero word) up to 128
+ *              entries.  Index j stands for used_out[j].
+ *  n_used_out  device int32: the number of distinct codes 0..242 present.
+ *  codes7      device uint8 [N][ceil(7 K / 8)]: bit q of the index of weight
+ *              (n, k) is bit 7 k + q of row n read as a little-endian bit
+ *              string (bit p in byte p / 8, position p % 8); the bits past
+ *              7 K are zero.
+ *  d_status    device int32; set to 0, then TQ_DATA_CODE for a byte
+ *              243..255 and TQ_DATA_ALPHABET for more than 128 distinct codes
+ *              (codes7 is then unspecified; memory stays in bounds).
+ *
+ * Four launches on `stream`: the first 32 bytes of used_out serve as a
+ * presence set until the list is written.  codes is read twice.
+ */
+int rb_truncate(const uint8_t* codes, int64_t N, int64_t K, uint8_t* used_out,
+                int32_t* n_used_out, uint8_t* codes7, int32_t* d_status, void* stream);
+
+/*
+ * rb_matmul7 -- Route B matmul over 7-bit indices (Route B paper, section
+ * 8.1, with the per-block books of section 8.3):
+ *
+ *     y[m, n] = alpha * rho_{n / rho_rows} * sum_k x[m, k] *
+ *               tables[n / table_rows][used[index(n, k)]]  (+ bias[n])
+ *
+ *  codes7      device uint8 [N][ceil(7 K / 8)] in rb_truncate's layout
+ *              (fastest with K % 512 == 0 and a 16-byte aligned pointer at
+ *              M <= 16, K % 32 == 0 and a 4-byte aligned pointer above).
+ *  used        device uint8 [128]: index -> code; codes 243..255 read zero.
+ *  tables, table_rows, alpha, row_scale, rho_rows, bias, y, y_dtype, stream
+ *              as in rb_matmul_blocks.
+ *
+ * M <= 16 runs a GEMV kernel with the two-term bf16 split of each book entry
+ * (K % 512 == 0 with 16-byte aligned indices and 4-byte aligned activations;
+ * a plain fp32 kernel otherwise); M > 16 runs the fp16 MFMA kernel of rb_matmul with its
+ * bf16 replay.  The accuracy is that of rb_matmul.
+ */
+int rb_matmul7(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes7, int64_t N,
+               const uint8_t* used, const float* tables, int32_t table_rows, float alpha,
+               const uint16_t* row_scale, int32_t rho_rows, const float* bias, void* y,
+               int32_t y_dtype, void* stream);
 
 /* Human-readable name of a tq_status value. */
 const char* tq_status_string(int status);

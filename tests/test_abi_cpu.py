@@ -206,3 +206,66 @@ def test_binding_refuses_wrong_tensors():
         dmm.tq_matmul(xb, torch.zeros(15 * 13, dtype=torch.uint8),
                       torch.zeros(16, dtype=torch.float16), 16, 64,
                       torch.zeros(1, 16, dtype=torch.float32))
+
+
+def test_rb_matmul_blocks_argument_errors():
+    f = lib.rb_matmul_blocks
+    # x, M, K, codes, N, tables, table_rows, alpha, row_scale, rho_rows, bias, y, y_dtype, stream
+    ok = [FAKE, 4, 64, FAKE, 64, FAKE, 32, ctypes.c_float(0.02), None, 1, None, FAKE, 0, None]
+    for tr in (16, 33, 48, 1):
+        bad = list(ok); bad[6] = tr
+        assert f(*bad) == TQ_ERR_UNSUPPORTED            # not a multiple of 32
+    bad = list(ok); bad[6] = -32
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[9] = 0
+    assert f(*bad) == TQ_ERR_SHAPE                      # rho_rows < 1
+    bad = list(ok); bad[5] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[5] = FAKE_ODD
+    assert f(*bad) == TQ_ERR_ALIGN
+    bad = list(ok); bad[12] = 7
+    assert f(*bad) == TQ_ERR_DTYPE
+    bad = list(ok); bad[4] = 0
+    assert f(*bad) == 0                                 # N = 0: no-op
+
+
+def test_rb_truncate_argument_errors():
+    f = lib.rb_truncate
+    # codes, N, K, used_out, n_used_out, codes7, d_status, stream
+    ok = [FAKE, 8, 64, FAKE, FAKE, FAKE, FAKE, None]
+    for i in (3, 4, 6):
+        bad = list(ok); bad[i] = None
+        assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[5] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[1] = -1
+    assert f(*bad) == TQ_ERR_SHAPE
+    bad = list(ok); bad[2] = 1 << 31
+    assert f(*bad) == TQ_ERR_SHAPE
+    for i in (3, 4, 6):
+        bad = list(ok); bad[i] = ctypes.c_void_p(0x10002)
+        assert f(*bad) == TQ_ERR_ALIGN                  # used_out, n_used_out, d_status
+
+
+def test_rb_matmul7_argument_errors():
+    f = lib.rb_matmul7
+    # x, M, K, codes7, N, used, tables, table_rows, alpha, row_scale, rho_rows, bias, y, dtype, stream
+    ok = [FAKE, 4, 64, FAKE, 64, FAKE, FAKE, 0, ctypes.c_float(0.02), None, 1, None, FAKE, 0, None]
+    bad = list(ok); bad[5] = None
+    assert f(*bad) == TQ_ERR_NULL                       # the used-code list
+    bad = list(ok); bad[7] = 20
+    assert f(*bad) == TQ_ERR_UNSUPPORTED
+    bad = list(ok); bad[6] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[3] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[1] = 0
+    assert f(*bad) == 0
+
+
+def test_status_string_new_flags():
+    assert dmm.TQ_DATA_ALPHABET == 8
+    text = open(HEADER).read()
+    assert re.search(r"TQ_DATA_ALPHABET\s*=\s*8", text)
