@@ -112,6 +112,14 @@ __device__ __forceinline__ bool range_ok(const Range& R) {
     return max(R.hi.x, R.hi.y) <= 0x477f && min(R.lo.x, R.lo.y) >= 0x36ff;
 }
 
+// Row block of workgroup bx in a grid of nb: consecutive workgroups go to
+// the 8 XCDs in turn, so when nb is a multiple of 8 each XCD is given one
+// contiguous range of blocks (its L2 and TLB then see an eighth of the
+// matrix); other grids keep the plain order.
+__device__ __forceinline__ int64_t xcd_block(int64_t bx, int64_t nb) {
+    return (nb % 8 == 0) ? (bx % 8) * (nb / 8) + bx / 8 : bx;
+}
+
 // Wave-uniform read of an SGPR-able value.
 __device__ __forceinline__ int readfirstlane(int v) {
     return __builtin_amdgcn_readfirstlane(v);

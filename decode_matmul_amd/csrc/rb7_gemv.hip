@@ -102,7 +102,7 @@ rb7_gemv_tiled_kernel(Params p) {
     const int tid = threadIdx.x;
     const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
-    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * 16;
     const int64_t ntiles = p.K / kTileK;          // >= 1: the launcher requires K >= kTileK
 
     // fetch: piece (lane % 28) of tile row 2 wave + lane / 28 (lanes 56..63
@@ -158,6 +158,8 @@ rb7_gemv_tiled_kernel(Params p) {
     // tile t goes to LDS buffer t & 1: the barrier after writing tile t also
     // orders every read of tile t - 2 (same buffer) before its overwrite
     auto step = [&](const Stage& S, int buf) {
+        // keep the next stage's work (it waits on younger loads) out of this step
+        __builtin_amdgcn_sched_barrier(0);
         unsigned char* tile = tiles[buf];
         if (writer) *(u32x4*)(tile + lrow * kPitch + 16 * lpiece) = S.c;
         __syncthreads();

@@ -25,6 +25,10 @@
 //    of one weight, A holds the activation twice in the same two slots, so
 //    one MFMA accumulates x*hi + x*lo = x*v for four weights per lane.
 //    A rows are the M <= 16 tokens; C columns are the 16 rows.
+//  * Tiled path: every workgroup walks K from the same end, so at any time
+//    the chip reads one column window of all rows (measured faster than
+//    staggered starts or free-running waves), and the row blocks are dealt
+//    out so that each XCD streams one contiguous eighth of the matrix.
 #include "common.h"
 
 namespace dmm {
@@ -321,7 +325,7 @@ rb_gemv_tiled_kernel(Params p) {
     const int tid = threadIdx.x;
     const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
     const int lane = tid & 63;
-    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * 16;
     const int64_t ntiles = p.K / kTileK;          // >= 1: the launcher requires K >= kTileK
 
     // tile row this lane fetches (clamped into range), 16 bytes at 16 (lane & 31)
@@ -371,6 +375,8 @@ rb_gemv_tiled_kernel(Params p) {
     // tile t goes to LDS buffer t & 1: the barrier after writing tile t also
     // orders every read of tile t - 2 (same buffer) before its overwrite
     auto step = [&](const Stage& S, int buf) {
+        // keep the next stage's work (it waits on younger loads) out of this step
+        __builtin_amdgcn_sched_barrier(0);
         unsigned char* tile = tiles[buf];
         *(u32x4*)(tile + lrow * kTilePitch + 16 * (lane & 31)) = u32x4{S.c.x, S.c.y, S.c.z, S.c.w};
         __syncthreads();
