@@ -27,7 +27,10 @@
 //    sum and the fp16 group scale is applied in fp32 afterwards.
 //  * The trit table has 16 copies in LDS, entry b of copy c at byte
 //    (b << 8) | (c << 3), so one v_perm of the code byte and the copy offset
-//    forms the address and the 16 lanes of a phase hit distinct banks.
+//    forms the address and the 16 lanes of a phase hit distinct banks.  Its
+//    256 entries are a compile-time constant; each thread reads one, ahead
+//    of every other load (memory counters retire in order, so a later read
+//    would wait for the whole code stream), and stores four copies.
 //  * Tile rows are padded to 8 mod 16 bytes so the 16 rows of a block start
 //    in distinct bank pairs.
 //  * Wave partials are kept per block in LDS and summed in a fixed order at
@@ -45,6 +48,7 @@ constexpr int kT = 64 * kW;             // threads per workgroup
 constexpr int kNB = 13;                 // code bytes per group of 64 trits
 constexpr int kNSB = 4;                 // blocks in flight (one block per thread slot)
 constexpr int kLutBytes = 256 * 256;    // entry b, copy c at (b << 8) | (c << 3)
+static_assert(kT == 4 * 256, "one thread per (trit-table entry, four copies)");
 
 struct RowsParams {
     const uint16_t* x;
@@ -73,9 +77,29 @@ struct RowsParams {
     int64_t e_codes, e_scales;   // bytes per expert in a code / scale plane
 };
 
-__device__ __forceinline__ uint32_t trit_hi(int d) {     // bf16 high byte of 2t, d = t + 1
-    return d == 2 ? 0x40u : (d == 0 ? 0xC0u : 0x00u);
+// bf16 high bytes of 2t for the five trits of byte b (t = digit - 1, digit q
+// of b in base 3 least significant first): trits 0..3 in .x, trit 4 in .y;
+// bytes 243..255 decode to zero.  Built at compile time.
+struct TritBytes {
+    uint32_t lo[256];
+    uint32_t hi[256];
+};
+constexpr TritBytes make_trit_bytes() {
+    TritBytes t{};
+    for (int b = 0; b < 243; ++b) {
+        int v = b;
+        uint32_t h[5] = {0, 0, 0, 0, 0};
+        for (int q = 0; q < 5; ++q) {
+            const int d = v % 3;
+            h[q] = d == 2 ? 0x40u : (d == 0 ? 0xC0u : 0x00u);
+            v /= 3;
+        }
+        t.lo[b] = h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24);
+        t.hi[b] = h[4];
+    }
+    return t;
 }
+__constant__ TritBytes kTritBytes = make_trit_bytes();
 
 // 16-byte chunk j of a block: where it comes from and where it goes.
 struct Chunk {
@@ -181,6 +205,9 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         if (ntok == 0) return;                   // whole workgroup: nothing routed here
     }
     const int npass = (ntok + 3) >> 2;
+    // the trit table entry of this thread, read ahead of every other load
+    const uint32_t tt_lo = kTritBytes.lo[tid >> 2], tt_hi = kTritBytes.hi[tid >> 2];
+    __builtin_amdgcn_sched_barrier(0);
 
     const int col = lane & 15;
     const int kb = lane >> 4;
@@ -260,19 +287,12 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     for (int d = 0; d < NSB; ++d) load(d, R[d]);
 
     // ---- trit table, 16 copies (first pass; read only after the first barrier)
-    if (pass == 0)
-    for (int i = tid; i < 256 * 16; i += kT) {
-        const int b = i >> 4, c = i & 15;
-        uint32_t lo = 0, hi = 0;
-        if (b < 243) {
-            int v = b;
-            uint32_t h[5];
+    if (pass == 0) {
+        // entry tid / 4, copies 4 (tid & 3) .. + 3
+        const uint2 e = make_uint2(tt_lo, tt_hi);
+        unsigned char* d = lut + (((tid >> 2) << 8) | ((4 * (tid & 3)) << 3));
 #pragma unroll
-            for (int q = 0; q < 5; ++q) { h[q] = trit_hi(v % 3); v /= 3; }
-            lo = h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24);
-            hi = h[4];
-        }
-        *(uint2*)(lut + ((b << 8) | (c << 3))) = make_uint2(lo, hi);
+        for (int c = 0; c < 4; ++c) *(uint2*)(d + 8 * c) = e;
     }
 
 #pragma unroll
