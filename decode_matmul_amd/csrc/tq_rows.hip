@@ -14,9 +14,12 @@
 //    rows and walks them in blocks of 16 (one MFMA column block).  A block's
 //    bytes (codes and scales, every plane) are fetched as 16-byte chunks by
 //    the whole workgroup, so each load instruction reads 1 KiB of one
-//    contiguous range.  Four blocks are in flight in registers; a block is
-//    written to one of two LDS tiles, then decoded while the next blocks
-//    arrive.
+//    contiguous range.  Four blocks are in flight in registers.  When the
+//    whole range is in flight (dense calls whose range has at most four
+//    blocks, 56 rows at N = 14336) every block is written to a tile of its
+//    own and one barrier precedes the decode of all of them, so each wave
+//    runs its quad of every block back to back; otherwise a block is written
+//    to one of two LDS tiles and decoded while the next blocks arrive.
 //  * Wave w owns the K-groups 4w .. 4w+3 (a quad) of every block, so its
 //    activations are loaded into registers once and reused for all blocks.
 //  * Decode and MFMA mapping as in the general kernel: lane l decodes group
@@ -62,6 +65,7 @@ struct RowsParams {
     int pitch;               // LDS bytes per tile code row (row bytes + 8)
     int spitch;              // LDS bytes per tile scale row (2 ng + 8)
     int tile_bytes;          // one LDS tile: planes * 16 * (pitch + spitch)
+    int all_tiles;           // every block of the range has its own tile (no ring)
     void* y;
     int y_dtype;
     // grouped experts: workgroup w owns rows [c * rows_per_wg, ...) of expert
@@ -160,7 +164,8 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
     unsigned char* tiles = dyn;                              // 2 tiles
-    float* red = (float*)(dyn + 2 * p.tile_bytes);           // [blocks][kW][64]
+    constexpr int NSB = SPB == 1 ? kNSB : kNSB - 1;          // blocks in flight
+    float* red = (float*)(dyn + (p.all_tiles ? NSB : 2) * p.tile_bytes);   // [blocks][kW][64]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -281,7 +286,6 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     __builtin_amdgcn_sched_barrier(0);     // activations are issued before the code stream
 
     // ---- the first NSB blocks (fewer in flight when a block takes two slots)
-    constexpr int NSB = SPB == 1 ? kNSB : kNSB - 1;
     u32x4 R[NSB][SPB];
 #pragma unroll
     for (int d = 0; d < NSB; ++d) load(d, R[d]);
@@ -382,9 +386,21 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         load(blk + NSB, Rb);
         if (blk < nb) compute(blk, blk & 1);
     };
-    for (int b0 = 0; b0 < nb; b0 += NSB) {
+    if (p.all_tiles) {
+        // the range fits in flight: every block to its own tile, one barrier,
+        // then each wave decodes its quad of all blocks back to back
 #pragma unroll
-        for (int d = 0; d < NSB; ++d) body(b0 + d, R[d]);
+        for (int d = 0; d < NSB; ++d)
+            if (d < nb) store(d, R[d]);
+        __syncthreads();
+#pragma unroll
+        for (int d = 0; d < NSB; ++d)
+            if (d < nb) compute(d, d);
+    } else {
+        for (int b0 = 0; b0 < nb; b0 += NSB) {
+#pragma unroll
+            for (int d = 0; d < NSB; ++d) body(b0 + d, R[d]);
+        }
     }
     __syncthreads();
 
@@ -470,11 +486,15 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     }
     p.rows_per_wg = (int)rpw;
     const int blocks = (int)((rpw + 15) / 16);
-    const size_t smem = 2 * (size_t)p.tile_bytes + (size_t)blocks * kW * 64 * sizeof(float);
-    if (smem + kLutBytes > (size_t)kLdsLimit) return false;
     const int chunks = a.planes * ((int)ng * kNB + 2 * (int)ng);
     const int spb = (chunks + kT - 1) / kT;
     if (spb > 2) return false;
+    const int nsb = spb == 1 ? kNSB : kNSB - 1;
+    const size_t red_bytes = (size_t)blocks * kW * 64 * sizeof(float);
+    p.all_tiles = !grouped && blocks <= nsb &&
+                  nsb * (size_t)p.tile_bytes + red_bytes + kLutBytes <= (size_t)kLdsLimit;
+    const size_t smem = (p.all_tiles ? nsb : 2) * (size_t)p.tile_bytes + red_bytes;
+    if (smem + kLutBytes > (size_t)kLdsLimit) return false;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
     p.ids = a.ids;
