@@ -252,27 +252,20 @@ def test_tq_matmul_prefill_shapes(dmm, M, N, K):
     tq_case(dmm, M, N, K, 64, 2, torch.bfloat16, seed=M + 9 * N + K, x_special=True)
 
 
-def test_tq_matmul_prefill_full_sampled(dmm):
-    """ternary_gemv weights (14336 x 4096) at M = 2048 tokens: 64 sampled
-    token rows against the oracle over all 14336 outputs."""
+def test_tq_matmul_prefill_full(dmm):
+    """ternary_gemv weights (14336 x 4096, the oracle's package) at M = 2048
+    tokens: every output against the oracle."""
     d = workloads.ternary_gemv(M=1)
-    cs, ss = dmm.packed_shape(14336, 4096, 64)
-    W = dev(d["W"])
-    c = torch.empty(cs, dtype=torch.uint8, device=DEV)
-    s = torch.empty(ss, dtype=torch.int16, device=DEV)
-    say("tq_pack ternary_gemv for prefill")
-    assert int(host(dmm.tq_pack(W, 64, 1, c, s))[0]) == 0
-    del W
+    c, s = oracle.quantize_pack(d["W"], 64)
     rng = np.random.default_rng(60)
     xb = workloads.bf16_bits(rng.standard_normal((2048, 4096)).astype(np.float32))
     y = torch.empty((2048, 14336), dtype=torch.bfloat16, device=DEV)
     say("tq_matmul prefill M=2048 N=14336 K=4096")
-    dmm.tq_matmul(dev(bits16(xb)), c, s, 14336, 64, y)
-    rows = np.sort(rng.choice(2048, 64, replace=False))
-    got = y_host(y)[rows]
-    w = oracle.ternary_weights(4096, 64, host(c), host(s).view(np.uint16))
-    y_ref, B = oracle.matmul_ref(xb[rows], w)
-    assert_bound(got, y_ref, B, "ternary prefill sampled", "bf16")
+    dmm.tq_matmul(dev(bits16(xb)), dev(c), dev(bits16(s)), 14336, 64, y)
+    got = y_host(y)
+    w = oracle.ternary_weights(4096, 64, c, s)
+    y_ref, B = oracle.matmul_ref(xb, w)
+    assert_bound(got, y_ref, B, "ternary prefill", "bf16")
 
 
 TQ_CASES = [
@@ -314,11 +307,11 @@ def test_tq_matmul_offset_views(dmm, code_off, x_off):
 
 
 def test_tq_matmul_ternary_gemv_full(dmm):
-    """ternary_gemv: 14336 x 4096 at M = 1, 4, 16, codes packed on the GPU."""
+    """ternary_gemv: 14336 x 4096 at M = 1, 4, 16 on the oracle's package
+    (the device pack of the same W is checked bit for bit by the pack tests)."""
     d = workloads.ternary_gemv()
     W, x = d["W"], d["x"]
-    (c, s), st = gpu_pack(dmm, W, 64, 1)
-    assert st == 0
+    c, s = oracle.quantize_pack(W, 64)
     w_hat = oracle.ternary_weights(4096, 64, c, s)
     cd, sd = dev(c), dev(bits16(s))
     for M in (1, 4, 16):
@@ -332,7 +325,7 @@ def test_tq_matmul_ternary_gemv_full(dmm):
 
 def test_tq_matmul_ternary_small_full(dmm):
     d = workloads.ternary_small()
-    (c, s), st = gpu_pack(dmm, d["W"], 64, 1)
+    c, s = oracle.quantize_pack(d["W"], 64)
     y_ref, B = oracle.matmul_ref(d["x"], oracle.ternary_weights(256, 64, c, s))
     y = torch.empty((1, 256), dtype=torch.float32, device=DEV)
     say("tq_matmul ternary_small")
@@ -462,8 +455,9 @@ def test_tq_matmul_moe_full_sampled(dmm):
     experts = sorted(set(ids.reshape(-1).tolist()))
     sample = experts[:: max(1, len(experts) // 8)][:8]
     for e in sample:
-        r = slice(e * 2048, (e + 1) * 2048)
-        w = oracle.ternary_weights(4096, 64, c1[r], s1[r], c2[r], s2[r])
+        # expected values from the oracle's own two planes of expert e
+        (o1, t1), (o2, t2) = oracle.two_plane(W[e], 64)
+        w = oracle.ternary_weights(4096, 64, o1, t1, o2, t2)
         tt, jj = np.nonzero(ids == e)
         y_ref, B = oracle.matmul_ref(x[tt], w)
         assert_bound(got[tt, jj], y_ref, B, f"moe expert {e}")
@@ -609,9 +603,9 @@ def test_rb_matmul_routeb_gemv_full(dmm):
             assert_bound(y_host(y), y_ref, B, f"routeb_gemv M={M}", stored_of(y))
 
 
-def test_rb_matmul_routeb_prefill_full_sampled(dmm):
-    """routeb_prefill: M = 2048, K = N = 8192 with row scales; 96 sampled
-    token rows checked against the oracle over all 8192 outputs."""
+def test_rb_matmul_routeb_prefill_full(dmm):
+    """routeb_prefill: M = 2048, K = N = 8192 with row scales; every output
+    against the oracle."""
     d = workloads.routeb_prefill()
     table = dmm.rb_table(d["ladder"])
     y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=DEV)
@@ -619,11 +613,9 @@ def test_rb_matmul_routeb_prefill_full_sampled(dmm):
     dmm.rb_matmul(dev(bits16(d["x"])), dev(d["codes"]), dev(table), d["alpha"], y,
                   dev(bits16(d["row_scale"])))
     got = y_host(y)
-    rows = np.sort(np.random.default_rng(0).choice(2048, 96, replace=False))
-    rows[0], rows[-1] = 0, 2047
     w = oracle.rb_weights(d["codes"], oracle.rb_table(d["ladder"]), d["alpha"], d["row_scale"])
-    y_ref, B = oracle.matmul_ref(d["x"][rows], w)
-    assert_bound(got[rows], y_ref, B, "routeb_prefill", "bf16")
+    y_ref, B = oracle.matmul_ref(d["x"], w)
+    assert_bound(got, y_ref, B, "routeb_prefill", "bf16")
 
 
 # ------------------------------------------------------------------ misc

@@ -149,8 +149,8 @@ def test_rb_matmul_blocks_one_book_is_rb_matmul(dmm):
 
 
 def test_rb_matmul_blocks_routeb_blocks_full(dmm):
-    """routeb_blocks: N = K = 8192, one ladder per 32 rows, M = 1 and 4 (all
-    outputs), and M = 2048 prefill on 48 sampled token rows."""
+    """routeb_blocks: N = K = 8192, one ladder per 32 rows, M = 1 and 4, and
+    the M = 2048 prefill; every output against the oracle."""
     d = workloads.routeb_blocks(M=2048)
     lib_t, ref_t = tables_pair(dmm, d["ladders"])
     w = oracle.rb_weights(d["codes"], ref_t, d["alpha"], table_rows=32)
@@ -164,11 +164,8 @@ def test_rb_matmul_blocks_routeb_blocks_full(dmm):
     y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=DEV)
     say("rb_matmul_blocks routeb_blocks M=2048")
     dmm.rb_matmul_blocks(dev(bits16(d["x"])), cd, td, 32, d["alpha"], y)
-    got = y_host(y)
-    rows = np.sort(np.random.default_rng(1).choice(2048, 48, replace=False))
-    rows[0], rows[-1] = 0, 2047
-    y_ref, B = oracle.matmul_ref(d["x"][rows], w)
-    assert_bound(got[rows], y_ref, B, "routeb_blocks M=2048", torch.bfloat16)
+    y_ref, B = oracle.matmul_ref(d["x"], w)
+    assert_bound(y_host(y), y_ref, B, "routeb_blocks M=2048", torch.bfloat16)
 
 
 # ------------------------------------------------------------ rb_truncate
@@ -337,8 +334,8 @@ def test_rb_matmul7_zero_k(dmm):
 
 
 def test_rb_matmul7_routeb_alphabet_full(dmm):
-    """routeb_alphabet: N = K = 8192 over 60 codes, M = 1 and 4 (all
-    outputs), M = 2048 on 48 sampled token rows."""
+    """routeb_alphabet: N = K = 8192 over 60 codes, M = 1 and 4, and the
+    M = 2048 prefill; every output against the oracle."""
     d = workloads.routeb_alphabet(M=2048)
     used, n_used, index = oracle.rb_truncate(d["codes"])
     packed = oracle.pack7(index)
@@ -354,8 +351,5 @@ def test_rb_matmul7_routeb_alphabet_full(dmm):
     y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=DEV)
     say("rb_matmul7 routeb_alphabet M=2048")
     dmm.rb_matmul7(dev(bits16(d["x"])), cd, 8192, ud, td, 0, d["alpha"], y)
-    got = y_host(y)
-    rows = np.sort(np.random.default_rng(3).choice(2048, 48, replace=False))
-    rows[0], rows[-1] = 0, 2047
-    y_ref, B = oracle.matmul_ref(d["x"][rows], w)
-    assert_bound(got[rows], y_ref, B, "routeb_alphabet M=2048", torch.bfloat16)
+    y_ref, B = oracle.matmul_ref(d["x"], w)
+    assert_bound(y_host(y), y_ref, B, "routeb_alphabet M=2048", torch.bfloat16)
