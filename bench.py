@@ -271,6 +271,10 @@ def main():
             "bytes_per_launch": bytes_launch,
             "us_per_launch": round(per_launch * 1e6, 3),
             "tok_s_equiv_per_layer": round(M / per_launch, 1),
+            # context: decode steps per second of a model whose packed weights
+            # (31.0 GB, the Route B page's Gemma 4 31B checkpoint) stream at
+            # this rate
+            "steps_per_s_31GB_model": round(achieved * 1e9 / 31.0e9, 1),
         },
     }
     del bufs, ys
