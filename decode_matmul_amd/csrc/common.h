@@ -160,7 +160,8 @@ struct TqMatmulArgs {
 };
 
 hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
-// Streaming dense form for M <= 4; false when the call is outside its domain.
+// Streaming form for a few tokens (dense M <= 4, or <= 16 when the codes stay
+// in LDS; grouped experts); false when the call is outside its domain.
 bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
 // MFMA prefill form for many tokens (dense, one plane, G = 64, M >= 128).
 bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);

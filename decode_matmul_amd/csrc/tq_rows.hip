@@ -5,8 +5,10 @@
 // "Five trits in a byte" and "Three values and a shared scale"; the second
 // plane follows the FUCINA README ("The method").
 //
-// This is the streaming form for M <= 4 tokens, where the time is the HBM read
-// of the package.  A row's codes (ng * 13 bytes) and scales (ng * 2 bytes)
+// This is the streaming form for a few tokens, where the time is the HBM read
+// of the package: dense calls with M <= 4, or up to 16 in passes of four when
+// every block of a workgroup's range stays in its LDS tile across the passes,
+// and grouped expert calls with any number of tokens per expert.  A row's codes (ng * 13 bytes) and scales (ng * 2 bytes)
 // are contiguous and consecutive rows follow each other, so a range of rows
 // is one contiguous byte range per array.
 //
@@ -159,7 +161,9 @@ __device__ __forceinline__ Chunk chunk_of(const RowsParams& p, int j) {
     return c;
 }
 
-template <int PL, int SPB, bool GR>
+// RU: a dense call of more than four tokens whose blocks all have tiles of
+// their own (passes after the first read no codes).
+template <int PL, int SPB, bool GR, bool RU>
 __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
@@ -286,9 +290,12 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     __builtin_amdgcn_sched_barrier(0);     // activations are issued before the code stream
 
     // ---- the first NSB blocks (fewer in flight when a block takes two slots)
+    // (dense passes after the first find every block still in its tile)
+    const bool reuse = RU && pass > 0;
     u32x4 R[NSB][SPB];
+    if (!reuse)
 #pragma unroll
-    for (int d = 0; d < NSB; ++d) load(d, R[d]);
+        for (int d = 0; d < NSB; ++d) load(d, R[d]);
 
     // ---- trit table, 16 copies (first pass; read only after the first barrier)
     if (pass == 0) {
@@ -389,9 +396,10 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     if (p.all_tiles) {
         // the range fits in flight: every block to its own tile, one barrier,
         // then each wave decodes its quad of all blocks back to back
+        if (!reuse)
 #pragma unroll
-        for (int d = 0; d < NSB; ++d)
-            if (d < nb) store(d, R[d]);
+            for (int d = 0; d < NSB; ++d)
+                if (d < nb) store(d, R[d]);
         __syncthreads();
 #pragma unroll
         for (int d = 0; d < NSB; ++d)
@@ -443,12 +451,13 @@ int compute_units() {
 
 // Streaming ternary GEMV; returns false (launching nothing) when the call is
 // outside its domain: G = 64, groups per row 16, 32, 48 or 64, 16-byte
-// aligned operands, LDS within the limit; dense calls with 1 <= M <= 4, or
-// grouped expert calls (any number of tokens per expert, in passes of four).
+// aligned operands, LDS within the limit; dense calls with 1 <= M <= 4 (up to
+// 16 when the range's blocks all have tiles of their own, so passes after the
+// first re-read no codes), or grouped expert calls (any number of tokens per
+// expert, in passes of four).
 bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     const bool grouped = a.n_experts > 0;
     if (a.G != 64 || a.M < 1 || a.N < 1) return false;
-    if (!grouped && a.M > 4) return false;
     const int64_t ng = a.K / 64;
     if (a.K % 64 != 0 || ng < 16 || ng % 16 != 0 || ng > 64) return false;
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
@@ -495,6 +504,7 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
                   nsb * (size_t)p.tile_bytes + red_bytes + kLutBytes <= (size_t)kLdsLimit;
     const size_t smem = (p.all_tiles ? nsb : 2) * (size_t)p.tile_bytes + red_bytes;
     if (smem + kLutBytes > (size_t)kLdsLimit) return false;
+    if (!grouped && (a.M > 16 || (a.M > 4 && !p.all_tiles))) return false;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
     p.ids = a.ids;
@@ -518,8 +528,9 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     const dim3 grid((unsigned)wgs), block(kT);
 #define DMM_ROWS(PL_, SPB_)                                                                \
     do {                                                                                   \
-        if (grouped) hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, true>), grid, block, smem, s, p); \
-        else hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, false>), grid, block, smem, s, p); \
+        if (grouped) hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, true, false>), grid, block, smem, s, p); \
+        else if (a.M > 4) hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, false, true>), grid, block, smem, s, p); \
+        else hipLaunchKernelGGL((tq_rows_kernel<PL_, SPB_, false, false>), grid, block, smem, s, p); \
     } while (0)
     if (a.planes == 1) {
         if (spb == 1) DMM_ROWS(1, 1);

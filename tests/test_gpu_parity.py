@@ -290,6 +290,9 @@ TQ_STREAM_CASES = [
     (1, 1000, 1024, 1), (2, 777, 2048, 2), (3, 300, 3072, 1), (4, 2050, 4096, 2),
     (1, 5, 4096, 1), (4, 4100, 4096, 1), (1, 20000, 1024, 1), (2, 33000, 1024, 1),
     (3, 1, 2048, 2),
+    # more than four tokens: passes over codes kept in LDS, or the general kernel
+    (5, 1000, 1024, 1), (8, 2050, 4096, 2), (12, 4100, 4096, 1), (16, 300, 3072, 1),
+    (13, 14336, 4096, 1), (8, 14336, 4096, 1), (16, 20000, 1024, 1), (7, 33000, 1024, 2),
 ]
 
 
