@@ -207,10 +207,35 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         const int v = i < p.total ? p.ids[i] : -1;
         return __builtin_amdgcn_ballot_w64(v == e);
     };
+    // One scan counts the expert's tokens and records its first four (token,
+    // slot) pairs, the first pass's rows; four chunks of ids are loaded before
+    // any of them is matched.
     int ntok = p.M;
+    int f0 = 0, f1 = 1, f2 = 2, f3 = 3;
     if constexpr (GR) {
         ntok = 0;
-        for (int i0 = 0; i0 < p.total; i0 += 64) ntok += __builtin_popcountll(match_mask(i0));
+        for (int i0 = 0; i0 < p.total; i0 += 256) {
+            int v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + 64 * u + lane;
+                v[u] = i < p.total ? p.ids[i] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint64_t m = __builtin_amdgcn_ballot_w64(v[u] == e);
+                while (m != 0ull && ntok < 4) {
+                    const int i = i0 + 64 * u + (int)__builtin_ctzll(m);
+                    if (ntok == 0) f0 = i;
+                    else if (ntok == 1) f1 = i;
+                    else if (ntok == 2) f2 = i;
+                    else f3 = i;
+                    ++ntok;
+                    m &= m - 1ull;
+                }
+                ntok += __builtin_popcountll(m);
+            }
+        }
         if (ntok == 0) return;                   // whole workgroup: nothing routed here
     }
     const int npass = (ntok + 3) >> 2;
@@ -258,6 +283,9 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     const int mt = min(4, ntok - 4 * pass);
     int o0 = 4 * pass, o1 = 4 * pass + 1, o2 = 4 * pass + 2, o3 = 4 * pass + 3;
     if constexpr (GR) {
+        if (pass == 0) { o0 = f0; o1 = f1; o2 = f2; o3 = f3; }
+    }
+    if (GR && pass > 0) {
         int k = 0;                         // matches before the current 64 ids
         for (int i0 = 0; i0 < p.total && k < 4 * pass + 4; i0 += 64) {
             uint64_t m = match_mask(i0);

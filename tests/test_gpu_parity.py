@@ -387,6 +387,11 @@ def test_tq_matmul_grouped_streaming(dmm):
     grouped_case(dmm, 3, 17, 3072, 2, 1, 1, seed=24)
     grouped_case(dmm, 4, 40, 1024, 5, 2, 2, seed=25, bad_ids=True, ydt=torch.bfloat16)
     grouped_case(dmm, 4, 40, 1024, 3, 2, 1, seed=26, bad_ids="all")
+    # several hundred (token, slot) ids: the routing scan takes them in steps of
+    # 256, an expert's first four matches can sit in different 64-id chunks,
+    # and every expert needs many passes of four
+    grouped_case(dmm, 6, 50, 1024, 100, 4, 1, seed=27, bad_ids=True)
+    grouped_case(dmm, 12, 24, 2048, 333, 3, 2, seed=28)
 
 
 def hot_case(dmm, E, N, K, T, top_k, n_hot, seed, bad_ids=False, ydt=torch.float32):
