@@ -189,10 +189,58 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
             return;
         }
     }
-    // work item: the row range, and (grouped) the expert
-    const int el = GR ? (int)blockIdx.x / p.chunks : 0;     // expert within the launch
+    // Work item: the row range and (grouped) the expert.  Grouped launches of
+    // at most 64 experts and 256 (token, slot) ids take their experts
+    // heaviest first (most passes of four tokens, then lowest index), so that
+    // an expert needing several passes starts in the first round instead of
+    // lengthening the last.  Every wave holds the ids in registers; wave 0
+    // counts the tokens of each expert in the partial buffer (idle until the
+    // first tile barrier) and ranks them, one ballot per pass count.
+    int el = GR ? (int)blockIdx.x / p.chunks : 0;            // expert within the launch
+    int vid[4] = {-1, -1, -1, -1};
+    const bool ids_in_regs = GR && p.total <= 256;
+    if constexpr (GR) {
+        if (ids_in_regs) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 64 * u + lane;
+                vid[u] = i < p.total ? p.ids[i] : -1;
+            }
+            const int nl = p.n_items / p.chunks;
+            if (nl > 1 && nl <= 64) {
+                int* cnt = (int*)red;
+                int* order = cnt + 64;
+                if (wave == 0) {
+                    // one wave counts, ranks and writes the order: its LDS
+                    // operations complete in issue order, so no barrier between
+                    cnt[lane] = 0;
+                    __builtin_amdgcn_wave_barrier();      // keep the three steps in this order
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int d = vid[u] - p.e_begin;
+                        if (d >= 0 && d < nl) atomicAdd(&cnt[d], 1);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    const int key = lane < nl ? (cnt[lane] + 3) >> 2 : -1;
+                    int kmax = key;
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, __shfl_xor(kmax, o));
+                    kmax = readfirstlane(kmax);
+                    int base = 0, rank = 0;
+                    for (int k = kmax; k >= 0; --k) {
+                        const uint64_t m = __builtin_amdgcn_ballot_w64(key == k);
+                        if (key == k) rank = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                        base += __builtin_popcountll(m);
+                    }
+                    if (lane < nl) order[rank] = lane;
+                }
+                __syncthreads();
+                el = order[el];
+            }
+        }
+    }
     const int e = GR ? p.e_begin + el : 0;
-    const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x - el * p.chunks : (int)blockIdx.x) * p.rows_per_wg;
+    const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x % p.chunks : (int)blockIdx.x) * p.rows_per_wg;
     const int64_t r1 = min(r0 + (int64_t)p.rows_per_wg, p.N);
     const int64_t rlast = r1 - 1;
     const int nb = (int)((r1 - r0 + 15) >> 4);
@@ -208,8 +256,8 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         return __builtin_amdgcn_ballot_w64(v == e);
     };
     // One scan counts the expert's tokens and records its first four (token,
-    // slot) pairs, the first pass's rows; four chunks of ids are loaded before
-    // any of them is matched.
+    // slot) pairs, the first pass's rows; four chunks of ids are matched at a
+    // time (from the registers when they hold every id).
     int ntok = p.M;
     int f0 = 0, f1 = 1, f2 = 2, f3 = 3;
     if constexpr (GR) {
@@ -219,7 +267,7 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = i0 + 64 * u + lane;
-                v[u] = i < p.total ? p.ids[i] : -1;
+                v[u] = ids_in_regs ? vid[u] : (i < p.total ? p.ids[i] : -1);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {

@@ -394,6 +394,16 @@ def test_tq_matmul_grouped_streaming(dmm):
     grouped_case(dmm, 12, 24, 2048, 333, 3, 2, seed=28)
 
 
+def test_tq_matmul_grouped_heavy_first(dmm):
+    """Launches of at most 64 experts and 256 ids take their experts in order
+    of passes (heaviest first): idle experts, experts of one to several passes
+    and equal pass counts in one launch; 65 experts keep the launch order."""
+    grouped_case(dmm, 64, 40, 1024, 30, 8, 1, seed=31)          # 240 ids, 0..9 tokens each
+    grouped_case(dmm, 8, 36, 2048, 40, 4, 2, seed=32, bad_ids=True)
+    grouped_case(dmm, 64, 24, 1024, 32, 8, 2, seed=33)          # exactly 256 ids
+    grouped_case(dmm, 65, 24, 1024, 20, 6, 1, seed=34)
+
+
 def hot_case(dmm, E, N, K, T, top_k, n_hot, seed, bad_ids=False, ydt=torch.float32):
     """tq_matmul_hot: plane 2 only for experts 0 .. n_hot - 1."""
     rng = np.random.default_rng(seed)
