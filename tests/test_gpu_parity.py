@@ -529,6 +529,8 @@ def test_rb_matmul_small(dmm, M, N, K):
 RB_TILED_CASES = [
     (1, 16, 512), (16, 17, 512), (3, 1000, 1536), (7, 33, 2560), (16, 4100, 1024),
     (2, 1, 3584), (12, 250, 5120), (1, 3, 512),
+    # 13 to 16 tokens stage the activations in LDS
+    (13, 333, 1536), (14, 48, 512), (15, 1000, 2048), (13, 16, 3584),
 ]
 
 
@@ -607,12 +609,13 @@ def test_rb_matmul_wide_code_book(dmm, M, N, K):
 
 
 def test_rb_matmul_routeb_gemv_full(dmm):
-    """routeb_gemv: N = K = 8192 at M = 1 and 4, fp32 and bf16 outputs."""
-    d = workloads.routeb_gemv()
+    """routeb_gemv: N = K = 8192 at M = 1, 4 and 16 (direct and LDS-staged
+    activations), fp32 and bf16 outputs."""
+    d = workloads.routeb_gemv(M=16)
     table = dmm.rb_table(d["ladder"])
     w = oracle.rb_weights(d["codes"], oracle.rb_table(d["ladder"]), d["alpha"])
     cd, td = dev(d["codes"]), dev(table)
-    for M in (1, 4):
+    for M in (1, 4, 16):
         y_ref, B = oracle.matmul_ref(d["x"][:M], w)
         for ydt in (torch.float32, torch.bfloat16):
             y = torch.empty((M, 8192), dtype=ydt, device=DEV)
