@@ -19,7 +19,8 @@ so host launch overhead is not timed.
                over a bounded sample of the same workload.
   extra        the other packed-matmul workloads, timed the same way (per
                launch, HIP events, rotating buffers): ternary GEMV at
-               M = 1, 4, 16, the two-plane MoE grouped GEMV, the Route B
+               M = 1, 4, 16 (and tq_pack / tq_unpack on its matrix, per
+               call), the two-plane MoE grouped GEMV, the Route B
                prefill at M = 2048 (TFLOP/s), Route B GEMV at M = 4.
 
 Inputs are the seeded synthetic workloads of workloads.py; the pages'
@@ -331,7 +332,18 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         s = torch.empty(ss, dtype=torch.int16, device=dev)
         st = dmm.tq_pack(W, 64, 1, c, s)
         assert int(st.item()) == 0
-        del W
+        # the packer and the unpacker on this matrix (W fp32, 234.9 MB)
+        pst = torch.zeros(1, dtype=torch.int32, device=dev)
+        c_again, s_again = torch.empty_like(c), torch.empty_like(s)
+        sec = _timed_launches(torch, lambda: dmm.tq_pack(W, 64, 1, c_again, s_again, status=pst), 1,
+                              use_graph, reps=10)
+        assert torch.equal(c_again, c) and torch.equal(s_again, s)   # packing is deterministic
+        res["tq_pack_ternary_gemv"] = _rec_bytes(W.numel() * 4 + c.numel() + s.numel() * 2, sec)
+        Wu = torch.empty((14336, 4096), dtype=torch.bfloat16, device=dev)
+        sec = _timed_launches(torch, lambda: dmm.tq_unpack(c, s, 14336, 4096, 64, Wu, status=pst), 1,
+                              use_graph, reps=10)
+        res["tq_unpack_ternary_gemv_bf16"] = _rec_bytes(c.numel() + s.numel() * 2 + Wu.numel() * 2, sec)
+        del W, Wu, c_again, s_again
         R = 37
         cc = [c] + [c.clone() for _ in range(R - 1)]
         sc = [s] + [s.clone() for _ in range(R - 1)]
@@ -505,6 +517,12 @@ def _prefill_rec(sec, flops):
         "tflops": round(flops / sec / 1e12, 2),
         "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
     }
+
+
+def _rec_bytes(bytes_call, sec):
+    gbs = bytes_call / sec / 1e9
+    return {"us_per_call": round(sec * 1e6, 2), "bytes_per_call": int(bytes_call),
+            "GBs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def _rec(bytes_launch, sec, M, flops):

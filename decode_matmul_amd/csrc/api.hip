@@ -43,7 +43,7 @@ int tq_pack(const float* W, int64_t rows, int64_t K, int32_t G, int32_t planes,
         !aligned(d_status, 4))
         return TQ_ERR_ALIGN;
     const int64_t groups = rows * ((K + G - 1) / G);
-    if (groups / 256 >= kMaxDim) return TQ_ERR_SHAPE;
+    if (groups / 128 >= kMaxDim) return TQ_ERR_SHAPE;   // grid: 128 or 256 groups a workgroup
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dmm::launch_status_clear(d_status, s);
     if (e != hipSuccess) return TQ_ERR_HIP;
@@ -80,7 +80,7 @@ int tq_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_
         !aligned(d_status, 4))
         return TQ_ERR_ALIGN;
     const int64_t groups = rows * ((K + G - 1) / G);
-    if (groups / 256 >= kMaxDim) return TQ_ERR_SHAPE;
+    if (groups / 128 >= kMaxDim) return TQ_ERR_SHAPE;   // grid: 128 or 256 groups a workgroup
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dmm::launch_status_clear(d_status, s);
     if (e != hipSuccess) return TQ_ERR_HIP;

@@ -10,10 +10,14 @@
 // README, "The method" (W ~ d1 T1 + d2 T2; plane 2 packs the residual of
 // plane 1).
 //
-// One thread owns one (row, group).  Packing is not on the timed path; the
-// kernel is written for bit-exactness: a sequential float64 sum, one
-// float64 division, one float64 -> fp16 rounding, and the exact threshold
-// |W| > s/2 in place of round(W/s).
+// One thread owns one (row, group); it is written for bit-exactness: a
+// sequential float64 sum, one float64 division, one float64 -> fp16
+// rounding, and the exact threshold |W| > s/2 in place of round(W/s).
+// A workgroup owns consecutive groups, whose weights are one contiguous
+// span of W (rows are contiguous): the span is moved between HBM and LDS
+// with coalesced accesses, and each thread works on its group in LDS (one
+// pad word per 64 floats, so the lanes' sequential walks hit distinct
+// banks).  The code bytes are staged in LDS as well and stored coalesced.
 #include "common.h"
 
 namespace dmm {
@@ -70,68 +74,139 @@ __device__ float quantize_group(ValFn val, int n, int nb, uint8_t* out_codes,
     return s;
 }
 
+constexpr int kStageFloats = 16384;                  // floats of W staged per workgroup
+constexpr int kStageBytes = 256 * 13;                 // code bytes per plane and workgroup
+
+// Groups per workgroup at group size G (64 or 128): 256 or 128.
+inline int groups_per_wg(int G) { return kStageFloats / G < kPackThreads ? kStageFloats / G : kPackThreads; }
+
+__device__ __forceinline__ int stage_idx(int64_t i) { return (int)(i + (i >> 6)); }
+
+// First element (in W's row-major order) of group gid, and its size.
+__device__ __forceinline__ int64_t group_start(int64_t gid, int64_t K, int G, int ng, int* n) {
+    const int64_t r = gid / ng;
+    const int64_t k0 = (gid - r * ng) * (int64_t)G;
+    *n = (int)((K - k0) < (int64_t)G ? (K - k0) : (int64_t)G);
+    return r * K + k0;
+}
+
 __global__ void __launch_bounds__(kPackThreads)
 pack_kernel(const float* __restrict__ W, int64_t rows, int64_t K, int G, int ng, int nb,
-            int planes, uint8_t* __restrict__ c1, uint16_t* __restrict__ s1,
+            int gpw, int planes, uint8_t* __restrict__ c1, uint16_t* __restrict__ s1,
             uint8_t* __restrict__ c2, uint16_t* __restrict__ s2, int32_t* st) {
-    int64_t gid = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
-    if (gid >= rows * (int64_t)ng) return;
-    int64_t r = gid / ng;
-    int g = (int)(gid - r * ng);
-    int64_t k0 = (int64_t)g * G;
-    int n = (int)((K - k0) < (int64_t)G ? (K - k0) : (int64_t)G);
-    const float* w = W + r * K + k0;
-
-    bool ok1 = true;
-    float sc1 = quantize_group([&](int j) { return w[j]; }, n, nb, c1 + gid * nb, s1 + gid, ok1);
-    if (!ok1) atomic_or_status(st, TQ_DATA_RANGE);
-    if (planes == 2) {
-        float sh1 = 0.5f * sc1;
-        bool sp1 = sc1 > 0.f && ok1;
-        // residual R = fl32(W - s1 t1): s1 t1 is exact, one fp32 rounding
-        auto res = [&](int j) {
-            float v = w[j];
-            int t = trit_of(v, sh1, sp1);
-            float st1 = t > 0 ? sc1 : (t < 0 ? -sc1 : 0.f);
-            return v - st1;
-        };
-        bool ok2 = true;
-        quantize_group(res, n, nb, c2 + gid * nb, s2 + gid, ok2);
-        if (!ok2) atomic_or_status(st, TQ_DATA_RANGE);
+    __shared__ float wl[kStageFloats + kStageFloats / 64];
+    __shared__ uint8_t cl[2][kStageBytes];
+    const int tid = threadIdx.x;
+    const int64_t total = rows * (int64_t)ng;
+    const int64_t g0 = (int64_t)blockIdx.x * gpw;
+    const int64_t g1 = g0 + gpw < total ? g0 + gpw : total;
+    int n_last;
+    const int64_t start = group_start(g0, K, G, ng, &n_last);
+    const int64_t len = group_start(g1 - 1, K, G, ng, &n_last) + n_last - start;   // <= gpw * G
+    if (((start | len) & 3) == 0 && ((uintptr_t)W & 15) == 0) {
+        // 16-byte loads; four consecutive floats never straddle a pad word
+        const float4* w4 = (const float4*)(W + start);
+        const int len4 = (int)(len >> 2);
+#pragma unroll 4
+        for (int i = tid; i < len4; i += kPackThreads) {
+            const float4 v = w4[i];
+            float* d = wl + stage_idx(4 * (int64_t)i);
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        }
+    } else {
+#pragma unroll 4
+        for (int64_t i = tid; i < len; i += kPackThreads) wl[stage_idx(i)] = W[start + i];
     }
+    __syncthreads();
+
+    const int64_t gid = g0 + tid;
+    if (tid < gpw && gid < g1) {
+        int n;
+        const int64_t o = group_start(gid, K, G, ng, &n) - start;
+        auto w = [&](int j) { return wl[stage_idx(o + j)]; };
+        bool ok1 = true;
+        const float sc1 = quantize_group(w, n, nb, cl[0] + tid * nb, s1 + gid, ok1);
+        if (!ok1) atomic_or_status(st, TQ_DATA_RANGE);
+        if (planes == 2) {
+            const float sh1 = 0.5f * sc1;
+            const bool sp1 = sc1 > 0.f && ok1;
+            // residual R = fl32(W - s1 t1): s1 t1 is exact, one fp32 rounding
+            auto res = [&](int j) {
+                const float v = w(j);
+                const int t = trit_of(v, sh1, sp1);
+                const float st1 = t > 0 ? sc1 : (t < 0 ? -sc1 : 0.f);
+                return v - st1;
+            };
+            bool ok2 = true;
+            quantize_group(res, n, nb, cl[1] + tid * nb, s2 + gid, ok2);
+            if (!ok2) atomic_or_status(st, TQ_DATA_RANGE);
+        }
+    }
+    __syncthreads();
+    const int64_t nbytes = (g1 - g0) * nb;
+    for (int64_t i = tid; i < nbytes; i += kPackThreads) c1[g0 * nb + i] = cl[0][i];
+    if (planes == 2)
+        for (int64_t i = tid; i < nbytes; i += kPackThreads) c2[g0 * nb + i] = cl[1][i];
 }
 
 __global__ void __launch_bounds__(kPackThreads)
 unpack_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-              int64_t rows, int64_t K, int G, int ng, int nb, void* __restrict__ out,
+              int64_t rows, int64_t K, int G, int ng, int nb, int gpw, void* __restrict__ out,
               int out_dtype, int32_t* st) {
-    int64_t gid = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
-    if (gid >= rows * (int64_t)ng) return;
-    int64_t r = gid / ng;
-    int g = (int)(gid - r * ng);
-    int64_t k0 = (int64_t)g * G;
-    int n = (int)((K - k0) < (int64_t)G ? (K - k0) : (int64_t)G);
-    const uint8_t* cb = codes + gid * nb;
-    float s = f16_bits_to_f32(scales[gid]);
-    int flags = 0;
-    for (int i = 0; i < nb; ++i) {
-        int b = cb[i];
-        if (b > 242) { flags |= TQ_DATA_CODE; b = 121; }
-        for (int q = 0; q < 5; ++q) {
-            int d = b % 3;
-            b /= 3;
-            int j = 5 * i + q;
-            if (j >= n) {
-                if (d != 1) flags |= TQ_DATA_PADDING;
-                continue;
+    __shared__ float wl[kStageFloats + kStageFloats / 64];
+    const int tid = threadIdx.x;
+    const int64_t total = rows * (int64_t)ng;
+    const int64_t g0 = (int64_t)blockIdx.x * gpw;
+    const int64_t g1 = g0 + gpw < total ? g0 + gpw : total;
+    int n_last;
+    const int64_t start = group_start(g0, K, G, ng, &n_last);
+    const int64_t len = group_start(g1 - 1, K, G, ng, &n_last) + n_last - start;
+
+    const int64_t gid = g0 + tid;
+    if (tid < gpw && gid < g1) {
+        int n;
+        const int64_t o = group_start(gid, K, G, ng, &n) - start;
+        const uint8_t* cb = codes + gid * nb;
+        const float s = f16_bits_to_f32(scales[gid]);
+        int flags = 0;
+        for (int i = 0; i < nb; ++i) {
+            int b = cb[i];
+            if (b > 242) { flags |= TQ_DATA_CODE; b = 121; }
+            for (int q = 0; q < 5; ++q) {
+                const int d = b % 3;
+                b /= 3;
+                const int j = 5 * i + q;
+                if (j >= n) {
+                    if (d != 1) flags |= TQ_DATA_PADDING;
+                    continue;
+                }
+                wl[stage_idx(o + j)] = d == 2 ? s : (d == 0 ? -s : 0.f);     // exact s * t
             }
-            float v = d == 2 ? s : (d == 0 ? -s : 0.f);     // exact s * t
-            int64_t idx = r * K + k0 + j;
-            if (out_dtype == 0) ((float*)out)[idx] = v;
-            else ((uint16_t*)out)[idx] = f32_to_bf16_rne(v);
+        }
+        if (flags) atomic_or_status(st, flags);
+    }
+    __syncthreads();
+    if (((start | len) & 3) == 0 && ((uintptr_t)out & (out_dtype == 0 ? 15 : 7)) == 0) {
+        // four values per store
+        const int len4 = (int)(len >> 2);
+#pragma unroll 4
+        for (int i = tid; i < len4; i += kPackThreads) {
+            const float* v = wl + stage_idx(4 * (int64_t)i);
+            if (out_dtype == 0) {
+                ((float4*)((float*)out + start))[i] = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                ((uint2*)((uint16_t*)out + start))[i] = make_uint2(lo, hi);
+            }
+        }
+    } else {
+        for (int64_t i = tid; i < len; i += kPackThreads) {
+            const float v = wl[stage_idx(i)];
+            if (out_dtype == 0) ((float*)out)[start + i] = v;
+            else ((uint16_t*)out)[start + i] = f32_to_bf16_rne(v);
         }
     }
-    if (flags) atomic_or_status(st, flags);
 }
 
 }  // namespace
@@ -148,9 +223,10 @@ hipError_t launch_pack(const float* W, int64_t rows, int64_t K, int G, int plane
     int nb = (G + 4) / 5;
     int64_t groups = rows * (int64_t)ng;
     if (groups == 0) return hipSuccess;
-    int64_t blocks = (groups + kPackThreads - 1) / kPackThreads;
+    const int gpw = groups_per_wg(G);
+    int64_t blocks = (groups + gpw - 1) / gpw;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(kPackThreads), 0, s, W, rows,
-                       K, G, ng, nb, planes, c1, s1, c2, s2, d_status);
+                       K, G, ng, nb, gpw, planes, c1, s1, c2, s2, d_status);
     return hipGetLastError();
 }
 
@@ -161,9 +237,10 @@ hipError_t launch_unpack(const uint8_t* codes, const uint16_t* scales, int64_t r
     int nb = (G + 4) / 5;
     int64_t groups = rows * (int64_t)ng;
     if (groups == 0) return hipSuccess;
-    int64_t blocks = (groups + kPackThreads - 1) / kPackThreads;
+    const int gpw = groups_per_wg(G);
+    int64_t blocks = (groups + gpw - 1) / gpw;
     hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(kPackThreads), 0, s, codes,
-                       scales, rows, K, G, ng, nb, out, out_dtype, d_status);
+                       scales, rows, K, G, ng, nb, gpw, out, out_dtype, d_status);
     return hipGetLastError();
 }
 

@@ -84,6 +84,11 @@ PACK_CASES = [
     ("single group 3x64", lambda: (np.random.default_rng(3).standard_normal((3, 64))).astype(np.float32), 64, 1),
     ("two-plane 64x320", lambda: (np.random.default_rng(4).standard_normal((64, 320)) * 0.02).astype(np.float32), 64, 2),
     ("two-plane ragged 9x200 G128", lambda: (np.random.default_rng(5).standard_normal((9, 200)) * 3).astype(np.float32), 128, 2),
+    # many workgroups of 256 (G = 64) or 128 (G = 128) groups: boundaries
+    # inside rows and next to ragged last groups
+    ("multi-workgroup ragged 300x700 G64", lambda: (np.random.default_rng(6).standard_normal((300, 700)) * 0.02).astype(np.float32), 64, 1),
+    ("multi-workgroup ragged 200x1000 G128 two-plane", lambda: (np.random.default_rng(7).standard_normal((200, 1000)) * 0.02).astype(np.float32), 128, 2),
+    ("multi-workgroup ragged 129x333 G64 two-plane", lambda: (np.random.default_rng(8).standard_normal((129, 333))).astype(np.float32), 64, 2),
 ]
 
 
@@ -161,7 +166,8 @@ def test_pack_full_moe_two_plane_sampled(dmm):
 
 # ------------------------------------------------------------------ unpack
 
-@pytest.mark.parametrize("rows,K,G", [(256, 256, 64), (11, 70, 64), (7, 300, 128), (1, 64, 64)])
+@pytest.mark.parametrize("rows,K,G", [(256, 256, 64), (11, 70, 64), (7, 300, 128), (1, 64, 64),
+                                      (300, 700, 64), (200, 1000, 128)])
 def test_unpack_bit_exact(dmm, rows, K, G):
     W = (np.random.default_rng(rows + K).standard_normal((rows, K)) * 0.02).astype(np.float32)
     c, s = oracle.quantize_pack(W, G)
