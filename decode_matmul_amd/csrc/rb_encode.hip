@@ -26,6 +26,10 @@
 // max on the bits of the non-negative float, which order like integers;
 // non-finite weights raise TQ_DATA_RANGE); one workgroup per row that
 // encodes it (the block's first row also writes rho_h).  W is read twice.
+// With one scale per row (rho_rows = 1, K <= 16384) a row needs only its own
+// maximum: one workgroup stages the row in LDS, takes its maximum and encodes
+// it (W read once), and a last small launch writes rho_n once the global
+// maximum is complete.  The arithmetic is the same, so are the codes.
 #include "common.h"
 
 namespace dmm {
@@ -129,6 +133,49 @@ __global__ void __launch_bounds__(kEncThreads) enc_rows_kernel(EncParams p) {
     }
 }
 
+constexpr int64_t kFusedMaxK = 16384;          // floats of a row staged in LDS
+
+// rho_rows = 1: row blockIdx.x staged in LDS, its maximum, then its codes.
+__global__ void __launch_bounds__(kEncThreads) enc_fused_row_kernel(EncParams p) {
+    extern __shared__ float wrow[];
+    __shared__ float red[kEncThreads / 64];
+    const int64_t n = blockIdx.x;
+    const float* row = p.W + n * p.K;
+    float m = 0.f;
+    bool finite = true;
+    for (int64_t k = threadIdx.x; k < p.K; k += kEncThreads) {
+        const float v = row[k];
+        wrow[k] = v;
+        const float a = fabsf(v);
+        finite = finite && (a <= 3.402823466e38f);
+        m = fmaxf(m, a);
+    }
+    const bool bad = __syncthreads_or(!finite) != 0;
+    const float rm = block_max(m, red);                 // its barrier also publishes wrow
+    if (threadIdx.x == 0) {
+        atomicMax((unsigned int*)p.alpha, __builtin_bit_cast(unsigned int, rm));
+        p.alpha[1 + n] = rm;                            // the row is its own block
+        if (bad) atomicOr(p.status, (int32_t)TQ_DATA_RANGE);
+    }
+    const double ds = (double)rm;
+    const bool pos = rm > 0.f;
+    uint8_t* out = p.codes + n * p.K;
+    for (int64_t k = threadIdx.x; k < p.K; k += kEncThreads) {
+        const double r0 = pos ? (double)wrow[k] / ds : 0.0;
+        out[k] = (uint8_t)encode_word(r0, p);
+    }
+}
+
+// rho_n = fp16(alpha_n / alpha) after every row's maximum is in.
+__global__ void enc_rho_kernel(EncParams p) {
+    const float alpha = p.alpha[0];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < p.N; h += stride) {
+        const double q = alpha > 0.f ? (double)p.alpha[1 + h] / (double)alpha : 0.0;
+        p.row_scale[h] = f64_to_f16_rne(q);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float zeta,
@@ -154,6 +201,15 @@ hipError_t launch_rb_encode(const float* W, int64_t N, int64_t K, const float* l
     p.alpha = alpha;
     p.row_scale = row_scale;
     p.status = status;
+    if (rho_rows == 1 && K <= kFusedMaxK) {
+        hipLaunchKernelGGL(enc_fused_row_kernel, dim3((unsigned)N), dim3(kEncThreads),
+                           (size_t)K * sizeof(float), s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t rg = (N + 255) / 256;
+        hipLaunchKernelGGL(enc_rho_kernel, dim3((unsigned)(rg < 1024 ? rg : 1024)), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(enc_rowmax_kernel, dim3((unsigned)N), dim3(kEncThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

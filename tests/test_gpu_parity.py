@@ -738,7 +738,9 @@ def encode_inputs(N, K, seed):
     return W
 
 
-ENCODE_SHAPES = [(1, 1), (3, 70), (17, 1000), (64, 4096), (300, 257)]
+# (3, 16384) is the longest row encoded in one pass with per-row scales;
+# (2, 16400) takes the two-pass form
+ENCODE_SHAPES = [(1, 1), (3, 70), (17, 1000), (64, 4096), (300, 257), (3, 16384), (2, 16400)]
 
 
 @pytest.mark.parametrize("N,K", ENCODE_SHAPES)
@@ -789,6 +791,11 @@ def test_rb_encode_zero_rows_empty_and_bad_values(dmm):
         alpha = torch.empty(1, dtype=torch.float32, device=DEV)
         say(f"rb_encode non-finite {bad}")
         st = dmm.rb_encode(dev(W2), S_LADDER, codes, alpha)
+        assert int(host(st)[0]) & 1
+        alpha = torch.empty(6, dtype=torch.float32, device=DEV)
+        rs = torch.empty(5, dtype=torch.float16, device=DEV)
+        say(f"rb_encode non-finite {bad}, per-row scales")
+        st = dmm.rb_encode(dev(W2), S_LADDER, codes, alpha, row_scale=rs)
         assert int(host(st)[0]) & 1
 
 
