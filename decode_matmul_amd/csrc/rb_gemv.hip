@@ -501,7 +501,7 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
     const bool tiled = a.K >= kTileK && (a.K % kTileK == 0) &&
                        (((uintptr_t)a.codes & 15) == 0) && (((uintptr_t)a.x & 3) == 0);
     if (tiled) {
-        if (a.M > 4)
+        if (a.M >= kXStageMinM)
             hipLaunchKernelGGL(rb_gemv_tiled_kernel<true>, dim3((unsigned)((a.N + 15) / 16)),
                                dim3(kTThreads), 0, s, p);
         else
