@@ -59,7 +59,7 @@ struct RowsParams {
     const uint16_t* x;
     int64_t K, N;
     int ng;                  // groups per row, a multiple of 16
-    int M;                   // tokens, 1..4
+    int M;                   // dense: tokens, 1..16 (passes of four); grouped: 0
     const uint8_t* base;     // plane-1 codes; the other arrays sit at byte offsets from it
     int64_t off_codes2, off_scales1, off_scales2;
     uint32_t mul_cc, mul_cpr, mul_sc, mul_spr;   // 2^32 / d + 1 for the chunk divisions
