@@ -21,7 +21,8 @@ so host launch overhead is not timed.
                launch, HIP events, rotating buffers): ternary GEMV at
                M = 1, 4, 16 (and tq_pack / tq_unpack on its matrix, per
                call), the two-plane MoE grouped GEMV, the Route B
-               prefill at M = 2048 (TFLOP/s), Route B GEMV at M = 4.
+               prefill at M = 2048 (TFLOP/s) with and without a workspace
+               (rb_matmul_ws), Route B GEMV at M = 4 and 16.
 
 Inputs are the seeded synthetic workloads of workloads.py; the pages'
 published numbers are end-to-end decode rates on other hardware, so
@@ -453,6 +454,13 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
         flops = 2.0 * 2048 * 8192 * 8192
         res["routeb_prefill_M2048"] = _prefill_rec(sec, flops)
+        # the same call with a workspace: the activations are converted once
+        # (a pre-pass kernel, inside the timed call) instead of per N-tile
+        ws = torch.empty(dmm.rb_prefill_workspace_bytes(2048, 8192), dtype=torch.uint8, device=dev)
+        fn = lambda: dmm.rb_matmul_ws(x, cd, table, 0, float(d["alpha"]), y, ws, rho)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        res["routeb_prefill_ws_M2048"] = _prefill_rec(sec, flops)
+        del ws
 
     if "blocks" in sel:
         progress("extra: routeb_blocks (one code book per 32 rows)")

@@ -29,7 +29,7 @@ TQ_DATA_ALPHABET = 8
 
 EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
            "rb_matmul", "rb_matmul_rho_block", "rb_matmul_blocks", "rb_truncate",
-           "rb_matmul7", "tq_status_string")
+           "rb_matmul7", "rb_matmul_ws", "rb_prefill_workspace_bytes", "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -58,10 +58,14 @@ _lib.rb_matmul_blocks.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i32, ctypes.c_f
 _lib.rb_truncate.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _p]
 _lib.rb_matmul7.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p, _i32, ctypes.c_float, _p, _i32,
                             _p, _p, _i32, _p]
+_lib.rb_matmul_ws.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i32, ctypes.c_float, _p, _i32,
+                              _p, _p, _i32, _p, _i64, _p]
+_lib.rb_prefill_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
 for _name in EXPORTS[:-1]:
     getattr(_lib, _name).restype = _i32
+_lib.rb_prefill_workspace_bytes.restype = _i64
 
 
 def tq_status_string(status):
@@ -289,6 +293,40 @@ def rb_matmul_blocks(x, codes, tables, table_rows, alpha, y, row_scale=None, bia
                                float(alpha), _ptr(row_scale), int(rho_rows), _ptr(bias), _ptr(y),
                                _ydtype(y), _stream(dev))
     _raise(rc, "rb_matmul_blocks")
+
+
+def rb_prefill_workspace_bytes(M, K):
+    """Bytes of the workspace rb_matmul_ws takes for [M, K] activations."""
+    n = int(_lib.rb_prefill_workspace_bytes(int(M), int(K)))
+    if n < 0:
+        raise ValueError(f"rb_prefill_workspace_bytes: bad shape {M} x {K}")
+    return n
+
+
+def rb_matmul_ws(x, codes, tables, table_rows, alpha, y, workspace, row_scale=None, bias=None,
+                 rho_rows=1):
+    """rb_matmul_blocks with a workspace (uint8 device tensor of at least
+    rb_prefill_workspace_bytes(M, K) bytes, or None) in which the prefill
+    converts the activations once per call."""
+    dev = x.device
+    M, K = x.shape
+    N = codes.shape[0]
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes, "codes", _U8, N * K, dev)
+    _tables(tables, N, table_rows, dev)
+    if row_scale is not None:
+        _need(row_scale, "row_scale", _H16, -(-N // int(rho_rows)) if rho_rows > 0 else N, dev)
+    if bias is not None:
+        _need(bias, "bias", _F32, N, dev)
+    _need(y, "y", (y.dtype,), M * N, dev)
+    nbytes = 0
+    if workspace is not None:
+        nbytes = workspace.numel()
+        _need(workspace, "workspace", _U8, nbytes, dev)
+    rc = _lib.rb_matmul_ws(_ptr(x), M, K, _ptr(codes), N, _ptr(tables), int(table_rows),
+                           float(alpha), _ptr(row_scale), int(rho_rows), _ptr(bias), _ptr(y),
+                           _ydtype(y), _ptr(workspace), nbytes, _stream(dev))
+    _raise(rc, "rb_matmul_ws")
 
 
 def rb7_row_bytes(K):

@@ -204,7 +204,7 @@ static int rb_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
                             const uint8_t* used, int64_t N, const float* table,
                             int32_t table_rows, float alpha, const uint16_t* row_scale,
                             int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
-                            void* stream) {
+                            void* stream, void* workspace = nullptr, int64_t workspace_bytes = 0) {
     if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
         return TQ_ERR_SHAPE;
     if (rho_rows < 1 || table_rows < 0) return TQ_ERR_SHAPE;
@@ -230,13 +230,32 @@ static int rb_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
     a.bias = bias;
     a.y = y;
     a.y_dtype = y_dtype;
+    a.workspace = nullptr;
     hipStream_t s = (hipStream_t)stream;
     if (M <= 16) {
         if ((N + 15) / 16 >= kMaxDim) return TQ_ERR_SHAPE;
         return hip_status(used ? dmm::launch_rb7_gemv(a, s) : dmm::launch_rb_gemv(a, s));
     }
     if ((M + 255) / 256 >= 65536) return TQ_ERR_SHAPE;
+    if (workspace) {
+        if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+        if (workspace_bytes < dmm::rb_prefill_ws_bytes(M, K)) return TQ_ERR_SHAPE;
+        a.workspace = workspace;
+    }
     return hip_status(dmm::launch_rb_prefill(a, s));
+}
+
+int64_t rb_prefill_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K < 0 || M >= kMaxDim || K >= kMaxDim) return -1;
+    return dmm::rb_prefill_ws_bytes(M, K);
+}
+
+int rb_matmul_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                 const float* tables, int32_t table_rows, float alpha, const uint16_t* row_scale,
+                 int32_t rho_rows, const float* bias, void* y, int32_t y_dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+    return rb_matmul_common(x, M, K, codes, nullptr, N, tables, table_rows, alpha, row_scale,
+                            rho_rows, bias, y, y_dtype, stream, workspace, workspace_bytes);
 }
 
 int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,

@@ -180,7 +180,16 @@ struct RbMatmulArgs {
     const float* bias;
     void* y;
     int y_dtype;
+    void* workspace;        // NULL, or rb_prefill_ws_bytes(M, K) bytes for the prefill's
+                            // pre-converted activations
 };
+
+// Workspace of a prefill with pre-converted activations: fp16 x [M][K], then
+// at a 256-byte boundary one flag word per (256-row block, 32-wide K-slice).
+inline int64_t rb_prefill_ws_flags_offset(int64_t M, int64_t K) { return (M * K * 2 + 255) / 256 * 256; }
+inline int64_t rb_prefill_ws_bytes(int64_t M, int64_t K) {
+    return rb_prefill_ws_flags_offset(M, K) + (M + 255) / 256 * ((K + 31) / 32) * 4;
+}
 
 // Bytes of one row of 7-bit indices.
 inline int64_t rb7_row_bytes(int64_t K) { return (7 * K + 7) / 8; }

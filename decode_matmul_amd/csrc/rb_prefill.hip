@@ -92,6 +92,11 @@ struct Params {
     const float* bias;
     void* y;
     int y_dtype;
+    // pre-converted activations (rb_matmul_ws): fp16 x with the chunks fp16
+    // cannot hold zeroed, and per (256-row block, K-slice) a flag that the
+    // slice holds such a chunk; NULL when the kernel converts x itself
+    const uint16_t* xf;
+    const uint32_t* xflags;                  // [ceil(M / 256)][ceil(K / 32)]: bit t = rows 32 t .. 32 t + 31
 };
 
 // Row j of slot h sits in LDS row 32 h + (j ^ row_swizzle(h)).
@@ -124,7 +129,7 @@ struct Slice {
 };
 
 // AL: 16-byte aligned activations and codes, K % 32 == 0.  C7: 7-bit indices.
-template <bool AL, bool C7>
+template <bool AL, bool C7, bool XF>
 __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     // one LDS block: the code book at address 0 (so a v_perm result is its
     // own address), two buffers of (activation, weight) tiles, a few words
@@ -219,13 +224,15 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     const uint32_t cofs = (uint32_t)((ch << 4) | ((((cj & 1) << 1) | cc) << 2));
     static_assert(XCH == 2 && CCH == 1, "chunk mapping");
 
-    auto gload = [&](int s, Slice& S) {
+    // from_xf: the fp16 pass of a call with pre-converted activations
+    auto gload = [&](int s, Slice& S, bool from_xf) {
         const int64_t k0 = (int64_t)min(s, nslices - 1) * BK;
         if constexpr (AL) {
+            const uint16_t* xs = (XF && from_xf) ? p.xf : p.x;
 #pragma unroll
             for (int i = 0; i < XCH; ++i) {
                 const int64_t m = min(m0 + xr + 128 * i, p.M - 1);
-                S.xa[i] = *(const u32x4*)(p.x + m * p.K + k0 + 8 * xc);
+                S.xa[i] = *(const u32x4*)(xs + m * p.K + k0 + 8 * xc);
             }
             const int64_t n = min(n0 + cr, p.N - 1);
             if constexpr (C7)      // 28 bytes per slice: dwords 0..3 or 3..6
@@ -307,6 +314,18 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     // does not fit fp16) is written as zeros and counted for the bf16 pass.
     auto store_f16 = [&](int s, int buf, const Slice& S, bool force_bad) {
         unsigned char* A = tiles2[2 * buf];
+        if constexpr (XF) {
+            // converted and flagged by the pre-pass (the replay list reads its flags)
+#pragma unroll
+            for (int i = 0; i < XCH; ++i) {
+                u32x4 v = S.xa[i];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[w] = force_bad ? 0u : v[w];
+                *(u32x4*)(A + (xr + 128 * i) * kPitch + 16 * xc) = v;
+            }
+            store_weights(buf, S, 0u, 0x05040100u);
+            return;
+        }
         int nbad = 0;
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
@@ -386,9 +405,11 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
 #pragma unroll
         for (int jn = 0; jn < NT; ++jn) F.b[jn] = *(const u32x4*)(B + brow[jn]);
     };
-    auto mfma_frag = [&](const Frag& F, bool f16) {
+    // tiles: bit i set = this wave's 32-row tile i takes part (uniform)
+    auto mfma_frag = [&](const Frag& F, bool f16, uint32_t tiles) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i) {
+            if (!((tiles >> i) & 1u)) continue;
 #pragma unroll
             for (int jn = 0; jn < NT; ++jn) {
                 if (f16)
@@ -400,6 +421,7 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
                         __builtin_bit_cast(bf16x8, F.a[i]), __builtin_bit_cast(bf16x8, F.b[jn]),
                         acc[i][jn], 0, 0, 0);
             }
+        }
     };
     static_assert(BK == 32, "two K-steps of 16 per slice");
 
@@ -414,11 +436,11 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     Slice S;
     Frag F0, F1;
     if (nslices > 0) {                     // K = 0 reads nothing (x may be null)
-        gload(0, S);
+        gload(0, S, true);
         store_f16(0, 0, S, all_bf16);
-        gload(1, S);
+        gload(1, S, true);
         store_f16(min(1, nslices - 1), 1, S, all_bf16);
-        gload(2, S);
+        gload(2, S, true);
     }
     __syncthreads();
     load_frag(0, 0, 0, F0);
@@ -426,15 +448,15 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     for (int s = 0; s < nslices; ++s) {
         const int buf = s & 1;
         load_frag(buf, buf, 1, F1);        // slice s, second K-step
-        mfma_frag(F0, true);
+        mfma_frag(F0, true, 0xFu);
         __syncthreads();                   // every wave is done reading buffer buf
         // decode slice s + 2 into buffer buf (past the end: the last slice
         // again, into a buffer nobody reads; no branch, so the decode
         // interleaves with the MFMAs)
         store_f16(min(s + 2, nslices - 1), buf, S, all_bf16);
         load_frag(buf ^ 1, buf ^ 1, 0, F0); // slice s + 1, first K-step
-        mfma_frag(F1, true);
-        gload(s + 3, S);                   // clamped; unused past the end
+        mfma_frag(F1, true, 0xFu);
+        gload(s + 3, S, true);             // clamped; unused past the end
     }
 
     // ---- bf16 pass over the chunks left out: the flagged slices below
@@ -446,8 +468,18 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     if (tid == 0) {
         int n = 0;
         const int mapped = min(nslices, kMapSlices);
-        for (int w = 0; w < mapped; ++w)
-            if (bad_map[w]) redo[n++] = (uint16_t)w;
+        if constexpr (XF) {
+            // the pre-pass flags of this 256-row block; later slices as one flag
+            const uint32_t* fr = p.xflags + (int64_t)blockIdx.y * nslices;
+            for (int w = 0; w < mapped; ++w)
+                if (all_bf16 || fr[w]) redo[n++] = (uint16_t)w;
+            bool late = false;
+            for (int w = kMapSlices; w < nslices; ++w) late = late || all_bf16 || fr[w] != 0u;
+            bad_map[kMapSlices] = late ? 1ull : 0ull;
+        } else {
+            for (int w = 0; w < mapped; ++w)
+                if (bad_map[w]) redo[n++] = (uint16_t)w;
+        }
         redo_n = n;
     }
     __syncthreads();
@@ -460,19 +492,28 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     auto replay_slice = [&](int r) {
         return r < nlist ? (int)readfirstlane(redo[r]) : kMapSlices + (r - nlist);
     };
-    if (nreplay > 0) gload(replay_slice(0), S);
+    if (nreplay > 0) gload(replay_slice(0), S, false);
 #pragma unroll 1
     for (int r = 0; r < nreplay; ++r) {
+        // with pre-pass flags, only this wave's 32-row tiles holding a chunk
+        // fp16 cannot hold take part (the others add zeros)
+        uint32_t tmask = 0xFu;
+        if constexpr (XF) {
+            if (!all_bf16) {
+                const uint32_t f = p.xflags[(int64_t)blockIdx.y * nslices + replay_slice(r)];
+                tmask = readfirstlane((f >> (wm * MT)) & 0xFu);
+            }
+        }
         store_bf16(0, S, all_bf16, 0);
         store_weights(1, S, 128u, 0x07060302u);
         __syncthreads();
-        gload(replay_slice(min(r + 1, nreplay - 1)), S);
+        gload(replay_slice(min(r + 1, nreplay - 1)), S, false);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             load_frag(0, 0, ks, F0);
-            mfma_frag(F0, false);
+            mfma_frag(F0, false, tmask);
             load_frag(0, 1, ks, F1);
-            mfma_frag(F1, false);
+            mfma_frag(F1, false, tmask);
         }
         __syncthreads();
     }
@@ -504,6 +545,53 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     }
 }
 
+// Pre-pass of rb_matmul_ws: bf16 x -> fp16, once per call instead of once per
+// N-tile workgroup.  A workgroup converts rows 256 by, columns 128 bx (four
+// K-slices); a chunk of 8 activations that fp16 cannot hold exactly becomes
+// zeros, and bit t of a slice's flag word says that rows 32 t .. 32 t + 31
+// of this row block hold such a chunk (the prefill replays those slices in
+// bf16, with the MFMAs of the flagged 32-row tiles only).  Every flag word
+// is written by exactly one workgroup, so nothing needs clearing first.
+constexpr int kXcRows = 256, kXcCols = 128;
+static_assert(kXcRows == BM && kXcCols % BK == 0, "flags per prefill row block and K-slice");
+__global__ void __launch_bounds__(256) xconv_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                   int64_t K, int64_t nsl,
+                                                   uint16_t* __restrict__ xf,
+                                                   uint32_t* __restrict__ flags) {
+    __shared__ uint32_t fl[kXcCols / BK];
+    const int tid = threadIdx.x;
+    if (tid < kXcCols / BK) fl[tid] = 0u;
+    __syncthreads();
+    const int64_t m0 = (int64_t)blockIdx.y * kXcRows;
+    const int cc = tid & 15;                              // chunk of 8 columns
+    const int64_t col = (int64_t)blockIdx.x * kXcCols + 8 * cc;
+    uint32_t tiles = 0u;                                  // 32-row tiles with a bad chunk
+    if (col < K) {                                        // K % 32 == 0: chunks are whole
+#pragma unroll 4
+        for (int i = 0; i < kXcRows / 16; ++i) {
+            const int64_t m = m0 + (tid >> 4) + 16 * i;
+            if (m < M) {
+                const u32x4 v = *(const u32x4*)(x + m * K + col);
+                Range R;
+                u32x4 o;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) o[w] = bf16x2_to_f16x2(v[w], R);
+                const bool bad = !range_ok(R);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) o[w] = bad ? 0u : o[w];
+                *(u32x4*)(xf + m * K + col) = o;
+                tiles |= (bad ? 1u : 0u) << (((tid >> 4) + 16 * i) >> 5);
+            }
+        }
+    }
+    if (tiles) atomicOr(&fl[cc >> 2], tiles);              // slice (col mod 128) / 32
+    __syncthreads();
+    if (tid < kXcCols / BK) {
+        const int64_t sl = (int64_t)blockIdx.x * (kXcCols / BK) + tid;
+        if (sl < nsl) flags[(int64_t)blockIdx.y * nsl + sl] = fl[tid];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s) {
@@ -530,12 +618,29 @@ hipError_t launch_rb_prefill(const RbMatmulArgs& a, hipStream_t s) {
     const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
     if (gx == 0 || gy == 0) return hipSuccess;
     const dim3 grid((unsigned)gx, (unsigned)gy), block(kThreads);
+    p.xf = nullptr;
+    p.xflags = nullptr;
+    if (a.workspace && aligned && a.K > 0) {
+        // activations converted once for the whole call
+        uint16_t* xf = (uint16_t*)a.workspace;
+        uint32_t* fl = (uint32_t*)((char*)a.workspace + rb_prefill_ws_flags_offset(a.M, a.K));
+        const int64_t nsl = (a.K + BK - 1) / BK;
+        hipLaunchKernelGGL(xconv_kernel, dim3((unsigned)((a.K + kXcCols - 1) / kXcCols), (unsigned)gy),
+                           dim3(256), 0, s, a.x, a.M, a.K, nsl, xf, fl);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.xf = xf;
+        p.xflags = fl;
+        if (a.used) hipLaunchKernelGGL((rb_prefill_kernel<true, true, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((rb_prefill_kernel<true, false, true>), grid, block, 0, s, p);
+        return hipGetLastError();
+    }
     if (a.used) {
-        if (aligned) hipLaunchKernelGGL((rb_prefill_kernel<true, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((rb_prefill_kernel<false, true>), grid, block, 0, s, p);
+        if (aligned) hipLaunchKernelGGL((rb_prefill_kernel<true, true, false>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((rb_prefill_kernel<false, true, false>), grid, block, 0, s, p);
     } else {
-        if (aligned) hipLaunchKernelGGL((rb_prefill_kernel<true, false>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((rb_prefill_kernel<false, false>), grid, block, 0, s, p);
+        if (aligned) hipLaunchKernelGGL((rb_prefill_kernel<true, false, false>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((rb_prefill_kernel<false, false, false>), grid, block, 0, s, p);
     }
     return hipGetLastError();
 }

@@ -292,6 +292,42 @@ int rb_matmul_blocks(const uint16_t* x, int64_t M, int64_t K, const uint8_t* cod
                      int32_t y_dtype, void* stream);
 
 /*
+ * rb_prefill_workspace_bytes -- bytes of the workspace rb_matmul_ws uses for
+ * an [M, K] activation matrix: an fp16 copy of x, then one flag word per
+ * 256-row block and 32-wide K-slice.  -1 for negative or too large sizes.
+ */
+int64_t rb_prefill_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * rb_matmul_ws -- rb_matmul_blocks with a caller-provided workspace that lets
+ * the prefill (M > 16) convert the activations once per call.
+ *
+ * The computation and the accuracy are those of rb_matmul_blocks (Route B
+ * paper, sections 3.2 and 3.3: y = alpha * rho_n * sum_k x[m, k] T[codes[n, k]]
+ * + bias_n; section 8.3 for several code books).  The prefill multiplies in
+ * fp16, and activations are exact in fp16 unless they fall outside
+ * [2^-17, 65280] in magnitude; such chunks are replayed in bf16.  Without a
+ * workspace, every N-tile workgroup converts its activation tile itself.
+ * With one, a first kernel converts x once and flags the K-slices holding
+ * chunks fp16 cannot hold, and the matmul reads the fp16 copy.
+ *
+ *  workspace        device memory of at least rb_prefill_workspace_bytes(M,
+ *                   K) bytes, 256-byte aligned (TQ_ERR_ALIGN), owned by the
+ *                   caller.  Its contents on entry do not matter, and it is
+ *                   overwritten.  NULL makes the call rb_matmul_blocks.
+ *  workspace_bytes  its size; smaller than required gives TQ_ERR_SHAPE.
+ *
+ * The workspace is used only by the prefill with 16-byte aligned x, 16-byte
+ * aligned codes and K % 32 == 0; otherwise it is ignored.  Calls that share a
+ * workspace must not overlap in time.  Every other argument and error is
+ * that of rb_matmul_blocks.
+ */
+int rb_matmul_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                 const float* tables, int32_t table_rows, float alpha, const uint16_t* row_scale,
+                 int32_t rho_rows, const float* bias, void* y, int32_t y_dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream);
+
+/*
  * rb_truncate -- the 7-bit truncated alphabet (Route B paper, section 8.1: a
  * layer that uses at most 128 of the 243 codes stores each weight in 7 bits,
  * plus a table from the 7-bit index to the code).

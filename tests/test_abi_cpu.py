@@ -25,7 +25,7 @@ FAKE_ODD = ctypes.c_void_p(0x10001)
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -269,3 +269,17 @@ def test_status_string_new_flags():
     assert dmm.TQ_DATA_ALPHABET == 8
     text = open(HEADER).read()
     assert re.search(r"TQ_DATA_ALPHABET\s*=\s*8", text)
+
+
+def test_rb_matmul_ws_workspace_checks():
+    """The prefill workspace: its size formula, and a misaligned or short
+    workspace rejected before any launch (M > 16 takes the prefill path)."""
+    M, K, N = 300, 1024, 64
+    nbytes = lib.rb_prefill_workspace_bytes(M, K)
+    want = (M * K * 2 + 255) // 256 * 256 + (-(-M // 256)) * (-(-K // 32)) * 4
+    assert nbytes == want
+    assert lib.rb_prefill_workspace_bytes(-1, K) == -1
+    ws_args = lambda ws, nb: (FAKE, M, K, FAKE, N, FAKE, 0, ctypes.c_float(1.0), None, 1, None,
+                              FAKE, 0, ws, nb, None)
+    assert lib.rb_matmul_ws(*ws_args(FAKE_ODD, nbytes)) == TQ_ERR_ALIGN
+    assert lib.rb_matmul_ws(*ws_args(FAKE, nbytes - 1)) == TQ_ERR_SHAPE

@@ -865,3 +865,110 @@ def test_rb_encode_large(dmm):
     W = encode_inputs(4096, 4096, seed=41)
     encode_case(dmm, W, S_LADDER, per_row=True)
     encode_case(dmm, W, S0_LADDER, per_row=False)
+
+
+# ----------------------------------------------- prefill with a workspace
+
+def ws_case(dmm, xb, codes, tables, table_rows, what, rs=None, rho_rows=1, ydt=torch.float32):
+    """rb_matmul_ws against the oracle, and bit for bit against the same call
+    without a workspace (the pre-pass converts and flags exactly what the
+    kernel would)."""
+    M, K = xb.shape
+    N = codes.shape[0]
+    xd, cd, td = dev(bits16(xb)), dev(codes), dev(tables.reshape(-1))
+    rsd = None if rs is None else dev(bits16(rs))
+    ws = torch.empty(dmm.rb_prefill_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)                                   # contents on entry do not matter
+    y_ws = torch.empty((M, N), dtype=ydt, device=DEV)
+    y_no = torch.empty((M, N), dtype=ydt, device=DEV)
+    say(f"rb_matmul_ws {what} M={M} N={N} K={K} table_rows={table_rows} y={ydt}")
+    dmm.rb_matmul_ws(xd, cd, td, table_rows, 0.02, y_ws, ws, rsd, None, rho_rows)
+    dmm.rb_matmul_blocks(xd, cd, td, table_rows, 0.02, y_no, rsd, None, rho_rows)
+    a, b = host(y_ws.view(torch.int16) if ydt == torch.bfloat16 else y_ws), \
+        host(y_no.view(torch.int16) if ydt == torch.bfloat16 else y_no)
+    assert np.array_equal(a, b), f"{what}: workspace and in-kernel conversion differ"
+    if table_rows:
+        blocks = [oracle.rb_weights(codes[h * table_rows:(h + 1) * table_rows], tables[h], np.float32(0.02),
+                                    None if rs is None else rs[h * table_rows // rho_rows:])
+                  for h in range(-(-N // table_rows))] if rho_rows == 1 or rs is None else None
+        w = np.concatenate(blocks) if blocks is not None else None
+    else:
+        w = oracle.rb_weights(codes, tables.reshape(243), np.float32(0.02),
+                              None if rs is None else np.repeat(rs, rho_rows)[:N])
+    if w is not None:
+        y_ref, B = oracle.matmul_ref(xb, w)
+        assert_bound(y_host(y_ws), y_ref, B, f"ws {what}", stored_of(y_ws))
+
+
+WS_SHAPES = [(17, 64, 64), (40, 50, 320), (300, 130, 512), (256, 520, 1024), (513, 96, 4128)]
+
+
+@pytest.mark.parametrize("M,N,K", WS_SHAPES)
+def test_rb_matmul_ws_shapes(dmm, M, N, K):
+    """Ragged M (partial 256-row blocks), K not a multiple of the pre-pass's
+    128 columns, fp32 and bf16 outputs, row scales."""
+    rng = np.random.default_rng(M + 7 * K)
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
+    rs = rng.uniform(0.5, 1.5, N).astype(np.float16).view(np.uint16)
+    ws_case(dmm, xb, codes, table, 0, "gaussian")
+    ws_case(dmm, xb, codes, table, 0, "gaussian, row scales", rs=rs, ydt=torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 64, 512), (40, 96, 1024)])
+def test_rb_matmul_ws_activations_outside_fp16(dmm, M, N, K):
+    """Chunks fp16 cannot hold (huge, tiny, a whole huge row) are flagged by
+    the pre-pass and replayed in bf16, as the in-kernel conversion does."""
+    rng = np.random.default_rng(5 * M + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    specials = np.array([1e5, -7e4, 3e-6, -1e-30, 0.0, 65536.0, 2.0 ** -17, 1e30], np.float32)
+    idx = rng.integers(0, M * K, 40)
+    x.reshape(-1)[idx] = specials[rng.integers(0, len(specials), 40)]
+    x[M // 2] *= np.float32(1e6)
+    xb = workloads.bf16_bits(x)
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
+    ws_case(dmm, xb, codes, table, 0, "outside fp16")
+    ws_case(dmm, xb, codes, table, 0, "outside fp16", ydt=torch.bfloat16)
+
+
+def test_rb_matmul_ws_blocks_small_m_and_errors(dmm):
+    """Per-block code books with a workspace; M <= 16 ignores it; a short
+    workspace is refused."""
+    rng = np.random.default_rng(91)
+    M, N, K = 100, 96, 512
+    xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+    tables = np.stack([oracle.rb_table((np.array([1.0, 0.33, 0.115, 0.037, 0.012]) *
+                                        rng.uniform(0.8, 1.2)).astype(np.float32)) for _ in range(3)])
+    ws_case(dmm, xb, codes, tables, 32, "per-block books")
+    xs = dev(bits16(xb[:4]))
+    ws = torch.empty(dmm.rb_prefill_workspace_bytes(4, K), dtype=torch.uint8, device=DEV)
+    y1 = torch.empty((4, N), dtype=torch.float32, device=DEV)
+    y2 = torch.empty((4, N), dtype=torch.float32, device=DEV)
+    say("rb_matmul_ws M=4 (GEMV)")
+    dmm.rb_matmul_ws(xs, dev(codes), dev(tables.reshape(-1)), 32, 0.02, y1, ws)
+    dmm.rb_matmul_blocks(xs, dev(codes), dev(tables.reshape(-1)), 32, 0.02, y2)
+    assert torch.equal(y1, y2)
+    short = torch.empty(dmm.rb_prefill_workspace_bytes(M, K) - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(Exception):
+        dmm.rb_matmul_ws(dev(bits16(xb)), dev(codes), dev(tables.reshape(-1)), 32, 0.02,
+                         torch.empty((M, N), dtype=torch.float32, device=DEV), short)
+
+
+def test_rb_matmul_ws_routeb_prefill_full(dmm):
+    """routeb_prefill (M = 2048, N = K = 8192, row scales) with a workspace:
+    bit for bit the in-kernel conversion's result."""
+    d = workloads.routeb_prefill()
+    M, K = d["x"].shape
+    N = d["codes"].shape[0]
+    xd, cd, td = dev(bits16(d["x"])), dev(d["codes"]), dev(dmm.rb_table(d["ladder"]))
+    rsd = dev(bits16(d["row_scale"]))
+    ws = torch.empty(dmm.rb_prefill_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    y_ws = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    y_no = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    say("rb_matmul_ws routeb_prefill M=2048")
+    dmm.rb_matmul_ws(xd, cd, td, 0, float(d["alpha"]), y_ws, ws, rsd)
+    dmm.rb_matmul(xd, cd, td, float(d["alpha"]), y_no, rsd)
+    assert torch.equal(y_ws.view(torch.int16), y_no.view(torch.int16))
