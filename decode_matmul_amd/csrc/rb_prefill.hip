@@ -347,11 +347,47 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
         store_weights(buf, S, 0u, 0x05040100u);
     };
 
+    // the bf16 pass's weights in one lookup per code: the book's (hi, lo)
+    // word gives the hi tile (buffer 0) and the lo tile (buffer 1)
+    auto store_weights_hilo = [&](const Slice& S) {
+        uint32_t F[4];
+        if constexpr (C7 && AL) {
+            const uint32_t sh = 16u * (uint32_t)cc;
+            F[0] = __builtin_amdgcn_alignbit(S.cd[0][1], S.cd[0][0], sh);
+            F[1] = __builtin_amdgcn_alignbit(S.cd[0][2], S.cd[0][1], sh);
+            F[2] = __builtin_amdgcn_alignbit(S.cd[0][3], S.cd[0][2], sh);
+            F[3] = S.cd[0][3] >> sh;
+        }
+        u32x4 h0, h1, l0, l1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t e[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                uint32_t a;
+                if constexpr (C7 && AL) a = index7_addr(F, 4 * w + b, cofs | 128u);
+                else a = perm_b32(S.cd[0][w], cofs | 128u, 0x0c0c0400u + ((uint32_t)b << 8));
+                e[b] = *(const uint32_t*)(lut + a);
+            }
+            const uint32_t h01 = perm_b32(e[1], e[0], 0x05040100u), h23 = perm_b32(e[3], e[2], 0x05040100u);
+            const uint32_t l01 = perm_b32(e[1], e[0], 0x07060302u), l23 = perm_b32(e[3], e[2], 0x07060302u);
+            if (w < 2) { h0[2 * w] = h01; h0[2 * w + 1] = h23; l0[2 * w] = l01; l0[2 * w + 1] = l23; }
+            else { h1[2 * w - 4] = h01; h1[2 * w - 3] = h23; l1[2 * w - 4] = l01; l1[2 * w - 3] = l23; }
+        }
+        unsigned char* dh = tiles2[1] + crs * kPitch + 32 * cc;
+        unsigned char* dl = tiles2[3] + crs * kPitch + 32 * cc;
+        *(u32x4*)dh = h0;
+        *(u32x4*)(dh + 16) = h1;
+        *(u32x4*)dl = l0;
+        *(u32x4*)(dl + 16) = l1;
+    };
+
     // the bf16 pass: bf16 activations of the chunks the fp16 pass left out
     // (zeros elsewhere) and the hi (part 0) or lo (part 1) bf16 weights
+    // (part -1: the activations alone)
     auto store_bf16 = [&](int buf, const Slice& S, bool force_bad, int part) {
         unsigned char* A = tiles2[2 * buf];
-        if (part == 0) {
+        if (part <= 0) {
 #pragma unroll
             for (int i = 0; i < XCH; ++i) {
                 Range R;
@@ -364,7 +400,7 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
                 *(u32x4*)(A + (xr + 128 * i) * kPitch + 16 * xc) = v;
             }
         }
-        store_weights(buf, S, 128u, part == 0 ? 0x05040100u : 0x07060302u);
+        if (part >= 0) store_weights(buf, S, 128u, part == 0 ? 0x05040100u : 0x07060302u);
     };
 
     // accumulators start life in the accumulation registers (the empty asm
@@ -504,8 +540,8 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
                 tmask = readfirstlane((f >> (wm * MT)) & 0xFu);
             }
         }
-        store_bf16(0, S, all_bf16, 0);
-        store_weights(1, S, 128u, 0x07060302u);
+        store_bf16(0, S, all_bf16, -1);                 // activations only
+        store_weights_hilo(S);
         __syncthreads();
         gload(replay_slice(min(r + 1, nreplay - 1)), S, false);
 #pragma unroll
