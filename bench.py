@@ -365,12 +365,13 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         fn = lambda: dmm.tq_matmul(xp, c, s, 14336, 64, yp)
         sec = _timed_launches(torch, fn, 1, use_graph, reps=5, warmup=1)
         flops = 2.0 * Mp * 14336 * 4096
-        res["ternary_prefill_M2048"] = {
-            "us_per_launch": round(sec * 1e6, 2),
-            "tflops": round(flops / sec / 1e12, 2),
-            "frac_bf16_mfma_peak": round(flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        }
-        del xp, yp
+        res["ternary_prefill_M2048"] = _prefill_rec(sec, flops)
+        # the same call with a workspace (activations converted once, inside the call)
+        wsp = torch.empty(dmm.tq_prefill_workspace_bytes(Mp, 4096), dtype=torch.uint8, device=dev)
+        fn = lambda: dmm.tq_matmul_ws(xp, c, s, 14336, 64, yp, wsp)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=5, warmup=1)
+        res["ternary_prefill_ws_M2048"] = _prefill_rec(sec, flops)
+        del xp, yp, wsp
 
     if "moe" in sel:
         progress("extra: moe_two_plane (generating 2 GiB of weights)")

@@ -29,7 +29,8 @@ TQ_DATA_ALPHABET = 8
 
 EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
            "rb_matmul", "rb_matmul_rho_block", "rb_matmul_blocks", "rb_truncate",
-           "rb_matmul7", "rb_matmul_ws", "rb_prefill_workspace_bytes", "tq_status_string")
+           "rb_matmul7", "rb_matmul_ws", "rb_prefill_workspace_bytes", "tq_matmul_ws",
+           "tq_prefill_workspace_bytes", "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -61,11 +62,14 @@ _lib.rb_matmul7.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p, _i32, ctypes.c_flo
 _lib.rb_matmul_ws.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i32, ctypes.c_float, _p, _i32,
                               _p, _p, _i32, _p, _i64, _p]
 _lib.rb_prefill_workspace_bytes.argtypes = [_i64, _i64]
+_lib.tq_matmul_ws.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p]
+_lib.tq_prefill_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
 for _name in EXPORTS[:-1]:
     getattr(_lib, _name).restype = _i32
 _lib.rb_prefill_workspace_bytes.restype = _i64
+_lib.tq_prefill_workspace_bytes.restype = _i64
 
 
 def tq_status_string(status):
@@ -183,6 +187,38 @@ def tq_matmul(x, codes1, scales1, N, G, y, codes2=None, scales2=None, n_experts=
                         N, G, n_experts, _ptr(expert_ids), top_k, _ptr(y), _ydtype(y),
                         _stream(dev))
     _raise(rc, "tq_matmul")
+
+
+def tq_prefill_workspace_bytes(M, K):
+    """Bytes of the workspace tq_matmul_ws takes for [M, K] activations."""
+    n = int(_lib.tq_prefill_workspace_bytes(int(M), int(K)))
+    if n < 0:
+        raise ValueError(f"tq_prefill_workspace_bytes: bad shape {M} x {K}")
+    return n
+
+
+def tq_matmul_ws(x, codes1, scales1, N, G, y, workspace, codes2=None, scales2=None):
+    """Dense tq_matmul with a workspace (uint8 device tensor of at least
+    tq_prefill_workspace_bytes(M, K) bytes, or None) in which the prefill
+    converts the activations once per call."""
+    dev = x.device
+    M, K = x.shape
+    cs, ss = packed_shape(N, K, G)
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes1, "codes1", _U8, cs[0] * cs[1] * cs[2], dev)
+    _need(scales1, "scales1", _H16, ss[0] * ss[1], dev)
+    if codes2 is not None or scales2 is not None:
+        _need(codes2, "codes2", _U8, cs[0] * cs[1] * cs[2], dev)
+        _need(scales2, "scales2", _H16, ss[0] * ss[1], dev)
+    _need(y, "y", (y.dtype,), M * N, dev)
+    nbytes = 0
+    if workspace is not None:
+        nbytes = workspace.numel()
+        _need(workspace, "workspace", _U8, nbytes, dev)
+    rc = _lib.tq_matmul_ws(_ptr(x), M, K, _ptr(codes1), _ptr(scales1), _ptr(codes2),
+                           _ptr(scales2), N, G, _ptr(y), _ydtype(y), _ptr(workspace), nbytes,
+                           _stream(dev))
+    _raise(rc, "tq_matmul_ws")
 
 
 def tq_matmul_hot(x, codes1, scales1, N, G, y, n_hot, n_experts, expert_ids, top_k,

@@ -93,7 +93,8 @@ static int tq_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
                             const uint16_t* scales1, const uint8_t* codes2,
                             const uint16_t* scales2, int32_t n_hot, int64_t N, int32_t G,
                             int32_t n_experts, const int32_t* expert_ids, int32_t top_k, void* y,
-                            int32_t y_dtype, void* stream) {
+                            int32_t y_dtype, void* stream, void* workspace = nullptr,
+                            int64_t workspace_bytes = 0) {
     if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
         return TQ_ERR_SHAPE;
     if (!group_ok(G)) return TQ_ERR_UNSUPPORTED;
@@ -132,6 +133,12 @@ static int tq_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
     a.e_begin = 0;
     a.e_end = n_experts;
     a.nan_rows = true;
+    a.workspace = nullptr;
+    if (workspace) {
+        if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
+        if (workspace_bytes < dmm::tq_prefill_ws_bytes(M, K)) return TQ_ERR_SHAPE;
+        a.workspace = workspace;
+    }
     hipStream_t s = (hipStream_t)stream;
     if (n_hot < 0 || n_hot == n_experts) return hip_status(dmm::launch_tq_matmul(a, s));
     if (n_hot == 0) {
@@ -161,6 +168,19 @@ int tq_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
               int32_t top_k, void* y, int32_t y_dtype, void* stream) {
     return tq_matmul_common(x, M, K, codes1, scales1, codes2, scales2, -1, N, G, n_experts,
                             expert_ids, top_k, y, y_dtype, stream);
+}
+
+int64_t tq_prefill_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K < 0 || M >= kMaxDim || K >= kMaxDim) return -1;
+    return dmm::tq_prefill_ws_bytes(M, K);
+}
+
+int tq_matmul_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
+                 const uint16_t* scales1, const uint8_t* codes2, const uint16_t* scales2,
+                 int64_t N, int32_t G, void* y, int32_t y_dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+    return tq_matmul_common(x, M, K, codes1, scales1, codes2, scales2, -1, N, G, 0, nullptr, 1, y,
+                            y_dtype, stream, workspace, workspace_bytes);
 }
 
 int tq_matmul_hot(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,

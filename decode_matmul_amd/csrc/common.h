@@ -157,7 +157,17 @@ struct TqMatmulArgs {
     int top_k;
     void* y;
     int y_dtype;
+    void* workspace;        // NULL, or tq_prefill_ws_bytes(M, K) bytes for the dense
+                            // prefill's pre-converted activations
 };
+
+// Workspace of a ternary prefill with pre-converted activations: fp16 x
+// [M][K], then at a 256-byte boundary one flag word per (128-row block,
+// group of 64 columns).
+inline int64_t tq_prefill_ws_flags_offset(int64_t M, int64_t K) { return (M * K * 2 + 255) / 256 * 256; }
+inline int64_t tq_prefill_ws_bytes(int64_t M, int64_t K) {
+    return tq_prefill_ws_flags_offset(M, K) + (M + 127) / 128 * ((K + 63) / 64) * 4;
+}
 
 hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
 // Streaming form for a few tokens (dense M <= 4, or <= 16 when the codes stay

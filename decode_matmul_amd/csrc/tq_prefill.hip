@@ -70,6 +70,11 @@ struct Params {
     const uint16_t* scales2;
     void* y;
     int y_dtype;
+    // pre-converted activations (tq_matmul_ws): fp16 x with the chunks fp16
+    // cannot hold zeroed, and per (128-row block, group) a flag that the group
+    // holds such a chunk; NULL when the kernel converts x itself
+    const uint16_t* xf;
+    const uint32_t* xflags;        // [ceil(M / 128)][ng]
 };
 
 // Per-thread loads of one K-slice: 2 chunks of 8 activations; 7 code bytes
@@ -105,6 +110,7 @@ __device__ __forceinline__ void trit_pairs(const uint32_t* El, const uint32_t* E
     }
 }
 
+template <bool XF>
 __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
     unsigned char* const lut = smem;
@@ -147,7 +153,8 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     const int64_t wrow = min(n0 + wr, p.N - 1);
     const int64_t row_bytes = (int64_t)p.ng * kNB;
 
-    auto gload = [&](int s, Slice& S) {
+    // from_xf: the fp16 pass of a call with pre-converted activations
+    auto gload = [&](int s, Slice& S, bool from_xf) {
         const int sc = min(s, nslices - 1);
         const int g = p.planes == 2 ? sc >> 1 : sc;
         const bool second = p.planes == 2 && (sc & 1);
@@ -156,7 +163,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int64_t m = min(m0 + xr0 + 64 * i, p.M - 1);
-            S.xa[i] = *(const u32x4*)(p.x + m * p.K + (int64_t)g * BK + xc);
+            S.xa[i] = *(const u32x4*)(((XF && from_xf) ? p.xf : p.x) + m * p.K + (int64_t)g * BK + xc);
         }
         const int64_t off = wrow * row_bytes + (int64_t)g * kNB + 6 * H;   // 7 bytes
         const int64_t a0 = off & ~(int64_t)3;
@@ -192,22 +199,28 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     auto store_f16 = [&](int s, int buf, const Slice& S) {
         unsigned char* X = bufs + buf * kBuf;
         unsigned char* Wt = X + kXTile;
-        int nbad = 0;
+        if constexpr (XF) {
+            // converted and flagged by the pre-pass (the replay list reads its flags)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            Range R;
-            u32x4 v;
+            for (int i = 0; i < 2; ++i) *(u32x4*)(X + (xr0 + 64 * i) * kPitch + 2 * xc) = S.xa[i];
+        } else {
+            int nbad = 0;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) v[w] = bf16x2_to_f16x2(S.xa[i][w], R);
-            const bool bad = !range_ok(R);
-            nbad += bad;
+            for (int i = 0; i < 2; ++i) {
+                Range R;
+                u32x4 v;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) v[w] = bad ? 0u : v[w];
-            *(u32x4*)(X + (xr0 + 64 * i) * kPitch + 2 * xc) = v;
+                for (int w = 0; w < 4; ++w) v[w] = bf16x2_to_f16x2(S.xa[i][w], R);
+                const bool bad = !range_ok(R);
+                nbad += bad;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[w] = bad ? 0u : v[w];
+                *(u32x4*)(X + (xr0 + 64 * i) * kPitch + 2 * xc) = v;
+            }
+            const bool wbad = __builtin_amdgcn_ballot_w64(nbad != 0) != 0;
+            unsigned char* fb = (unsigned char*)&bad_map[min(s, kMapSlices)] + wave;
+            *fb = (unsigned char)((s >= kMapSlices ? *fb : 0) | (wbad ? 1 : 0));
         }
-        const bool wbad = __builtin_amdgcn_ballot_w64(nbad != 0) != 0;
-        unsigned char* fb = (unsigned char*)&bad_map[min(s, kMapSlices)] + wave;
-        *fb = (unsigned char)((s >= kMapSlices ? *fb : 0) | (wbad ? 1 : 0));
         uint32_t P[16];
         decode_pairs(S, P);
         const f16x2 s2 = {__builtin_bit_cast(_Float16, (uint16_t)S.sc),
@@ -312,16 +325,16 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     // is decoded into the other buffer and slice s + 2 is loaded
     Slice S;
     if (nslices > 0) {
-        gload(0, S);
+        gload(0, S, true);
         store_f16(0, 0, S);
-        gload(1, S);
+        gload(1, S, true);
     }
     __syncthreads();
 #pragma unroll 1
     for (int s = 0; s < nslices; ++s) {
         const int buf = s & 1;
         if (s + 1 < nslices) store_f16(s + 1, buf ^ 1, S);
-        gload(s + 2, S);                   // clamped; unused past the end
+        gload(s + 2, S, true);             // clamped; unused past the end
         Frag F0, F1;
         load_frag(buf, buf, 0, F0);
         load_frag(buf, buf, 1, F1);
@@ -341,6 +354,16 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     if (tid == 0) {
         int n = 0;
         const int mapped = min(nslices, kMapSlices);
+        if constexpr (XF) {
+            // the pre-pass flags of this 128-row block (one per group: both
+            // planes of a group share its activations); later slices as one flag
+            const uint32_t* fr = p.xflags + (int64_t)blockIdx.y * p.ng;
+            for (int w = 0; w < mapped; ++w)
+                if (fr[p.planes == 2 ? w >> 1 : w]) redo[n++] = (uint16_t)w;
+            bool late = false;
+            for (int w = kMapSlices; w < nslices; ++w) late = late || fr[p.planes == 2 ? w >> 1 : w] != 0u;
+            bad_map[kMapSlices] = late ? 1ull : 0ull;
+        } else
         for (int w = 0; w < mapped; ++w)
             if (bad_map[w]) redo[n++] = (uint16_t)w;
         redo_n = n;
@@ -352,12 +375,12 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     auto replay_slice = [&](int r) {
         return r < nlist ? (int)readfirstlane(redo[r]) : kMapSlices + (r - nlist);
     };
-    if (nreplay > 0) gload(replay_slice(0), S);
+    if (nreplay > 0) gload(replay_slice(0), S, false);
 #pragma unroll 1
     for (int r = 0; r < nreplay; ++r) {
         store_bf16(S);
         __syncthreads();
-        gload(replay_slice(min(r + 1, nreplay - 1)), S);
+        gload(replay_slice(min(r + 1, nreplay - 1)), S, false);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             Frag F0, F1;
@@ -390,6 +413,51 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     }
 }
 
+// Pre-pass of tq_matmul_ws: bf16 x -> fp16, once per call instead of once per
+// N-tile workgroup (and per plane).  A workgroup converts rows 128 by,
+// columns 128 bx (two groups); a chunk of 8 activations that fp16 cannot hold
+// exactly becomes zeros, and a group's flag says whether any of its chunks
+// in this row block did (the prefill replays that group in bf16).  Every
+// flag word is written by exactly one workgroup.
+constexpr int kXcCols = 128;
+static_assert(kXcCols % BK == 0 && BM == 128, "flags per prefill row block and group");
+__global__ void __launch_bounds__(256) tq_xconv_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                      int64_t K, int ng, uint16_t* __restrict__ xf,
+                                                      uint32_t* __restrict__ flags) {
+    __shared__ uint32_t fl[kXcCols / BK];
+    const int tid = threadIdx.x;
+    if (tid < kXcCols / BK) fl[tid] = 0u;
+    __syncthreads();
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int cc = tid & 15;                              // chunk of 8 columns
+    const int64_t col = (int64_t)blockIdx.x * kXcCols + 8 * cc;
+    bool bad_any = false;
+    if (col < K) {                                        // K % 64 == 0: chunks are whole
+#pragma unroll 4
+        for (int i = 0; i < BM / 16; ++i) {
+            const int64_t m = m0 + (tid >> 4) + 16 * i;
+            if (m < M) {
+                const u32x4 v = *(const u32x4*)(x + m * K + col);
+                Range R;
+                u32x4 o;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) o[w] = bf16x2_to_f16x2(v[w], R);
+                const bool bad = !range_ok(R);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) o[w] = bad ? 0u : o[w];
+                *(u32x4*)(xf + m * K + col) = o;
+                bad_any = bad_any || bad;
+            }
+        }
+    }
+    if (bad_any) atomicOr(&fl[cc >> 3], 1u);              // group (col mod 128) / 64
+    __syncthreads();
+    if (tid < kXcCols / BK) {
+        const int64_t g = (int64_t)blockIdx.x * (kXcCols / BK) + tid;
+        if (g < ng) flags[(int64_t)blockIdx.y * ng + g] = fl[tid];
+    }
+}
+
 }  // namespace
 
 // Dense ternary matmul for many tokens; false (nothing launched) outside its
@@ -418,7 +486,22 @@ bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.scales2 = a.planes == 2 ? a.scales[1] : a.scales[0];
     p.y = a.y;
     p.y_dtype = a.y_dtype;
-    hipLaunchKernelGGL(tq_prefill_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s, p);
+    p.xf = nullptr;
+    p.xflags = nullptr;
+    if (a.workspace) {
+        // activations converted once for the whole call
+        uint16_t* xf = (uint16_t*)a.workspace;
+        uint32_t* fl = (uint32_t*)((char*)a.workspace + tq_prefill_ws_flags_offset(a.M, a.K));
+        hipLaunchKernelGGL(tq_xconv_kernel, dim3((unsigned)((a.K + kXcCols - 1) / kXcCols), (unsigned)gy),
+                           dim3(256), 0, s, a.x, a.M, a.K, p.ng, xf, fl);
+        *err = hipGetLastError();
+        if (*err != hipSuccess) return true;
+        p.xf = xf;
+        p.xflags = fl;
+        hipLaunchKernelGGL(tq_prefill_kernel<true>, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(tq_prefill_kernel<false>, dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s, p);
+    }
     *err = hipGetLastError();
     return true;
 }

@@ -144,6 +144,42 @@ int tq_matmul(const uint16_t* x, int64_t M, int64_t K,
               int32_t top_k, void* y, int32_t y_dtype, void* stream);
 
 /*
+ * tq_prefill_workspace_bytes -- bytes of the workspace tq_matmul_ws uses for
+ * an [M, K] activation matrix: an fp16 copy of x, then one flag word per
+ * 128-row block and group of 64 columns.  -1 for negative or too large sizes.
+ */
+int64_t tq_prefill_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * tq_matmul_ws -- dense tq_matmul (n_experts = 0) with a caller-provided
+ * workspace that lets the prefill (M >= 128, G = 64) convert the activations
+ * once per call.
+ *
+ * The computation and the accuracy are those of tq_matmul (pack-unpack-run,
+ * "Three values and a shared scale": W_hat = s * t per group; FUCINA README,
+ * "The method", for two planes).  The prefill multiplies in fp16, and
+ * activations are exact in fp16 unless they fall outside [2^-17, 65280] in
+ * magnitude; such chunks are replayed in bf16.  Without a workspace, every
+ * N-tile workgroup converts its activation tile itself, once per plane.
+ * With one, a first kernel converts x once and flags the groups holding
+ * chunks fp16 cannot hold.  The output is bit for bit that of tq_matmul.
+ *
+ *  workspace        device memory of at least tq_prefill_workspace_bytes(M,
+ *                   K) bytes, 256-byte aligned (TQ_ERR_ALIGN), owned by the
+ *                   caller.  Its contents on entry do not matter, and it is
+ *                   overwritten.  NULL makes the call tq_matmul.
+ *  workspace_bytes  its size; smaller than required gives TQ_ERR_SHAPE.
+ *
+ * The workspace is used only when the call takes the prefill kernel; otherwise
+ * it is ignored.  Calls that share a workspace must not overlap in time.
+ * Every other argument and error is that of tq_matmul.
+ */
+int tq_matmul_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes1,
+                 const uint16_t* scales1, const uint8_t* codes2, const uint16_t* scales2,
+                 int64_t N, int32_t G, void* y, int32_t y_dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream);
+
+/*
  * tq_matmul_hot -- grouped two-plane experts with a hot prefix (FUCINA
  * README, "The method": hot experts get both planes and cold experts one,
  * and experts are stored hot-first so that the second plane covers the

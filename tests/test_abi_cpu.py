@@ -283,3 +283,16 @@ def test_rb_matmul_ws_workspace_checks():
                               FAKE, 0, ws, nb, None)
     assert lib.rb_matmul_ws(*ws_args(FAKE_ODD, nbytes)) == TQ_ERR_ALIGN
     assert lib.rb_matmul_ws(*ws_args(FAKE, nbytes - 1)) == TQ_ERR_SHAPE
+
+
+def test_tq_matmul_ws_workspace_checks():
+    """The ternary prefill workspace: its size formula, and a misaligned or
+    short workspace rejected before any launch."""
+    M, K, N = 300, 1024, 64
+    nbytes = lib.tq_prefill_workspace_bytes(M, K)
+    want = (M * K * 2 + 255) // 256 * 256 + (-(-M // 128)) * (-(-K // 64)) * 4
+    assert nbytes == want
+    assert lib.tq_prefill_workspace_bytes(M, -1) == -1
+    args = lambda ws, nb: (FAKE, M, K, FAKE, FAKE, None, None, N, 64, FAKE, 0, ws, nb, None)
+    assert lib.tq_matmul_ws(*args(FAKE_ODD, nbytes)) == TQ_ERR_ALIGN
+    assert lib.tq_matmul_ws(*args(FAKE, nbytes - 1)) == TQ_ERR_SHAPE

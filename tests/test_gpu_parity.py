@@ -972,3 +972,78 @@ def test_rb_matmul_ws_routeb_prefill_full(dmm):
     dmm.rb_matmul_ws(xd, cd, td, 0, float(d["alpha"]), y_ws, ws, rsd)
     dmm.rb_matmul(xd, cd, td, float(d["alpha"]), y_no, rsd)
     assert torch.equal(y_ws.view(torch.int16), y_no.view(torch.int16))
+
+
+def tq_ws_case(dmm, M, N, K, planes, ydt, seed, x_special=False):
+    """tq_matmul_ws against the oracle, and bit for bit against tq_matmul."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    if x_special:
+        xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = 3.0e-7
+        xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = -7.0e4
+        xf[rng.integers(0, M, 20), rng.integers(0, K, 20)] = 0.0
+        xf[M // 2] *= np.float32(1e6)
+    xb = workloads.bf16_bits(xf)
+    if planes == 1:
+        c1, s1 = oracle.quantize_pack(W, 64)
+        c2 = s2 = None
+    else:
+        (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    xd = dev(bits16(xb))
+    args = (dev(c1), dev(bits16(s1)), N, 64)
+    extra = (None if c2 is None else dev(c2), None if s2 is None else dev(bits16(s2)))
+    ws = torch.empty(dmm.tq_prefill_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    ws.fill_(0x5A)                                   # contents on entry do not matter
+    y_ws = torch.empty((M, N), dtype=ydt, device=DEV)
+    y_no = torch.empty((M, N), dtype=ydt, device=DEV)
+    say(f"tq_matmul_ws M={M} N={N} K={K} planes={planes} y={ydt} special={x_special}")
+    dmm.tq_matmul_ws(xd, *args, y_ws, ws, *extra)
+    dmm.tq_matmul(xd, *args, y_no, *extra)
+    v = (lambda t: t.view(torch.int16)) if ydt == torch.bfloat16 else (lambda t: t)
+    assert torch.equal(v(y_ws), v(y_no)), "workspace and in-kernel conversion differ"
+    y_ref, B = oracle.matmul_ref(xb, oracle.ternary_weights(K, 64, c1, s1, c2, s2))
+    assert_bound(y_host(y_ws), y_ref, B, f"tq ws M={M} N={N} K={K}", stored_of(y_ws))
+
+
+@pytest.mark.parametrize("M,N,K", TQ_PREFILL_CASES + [(1000, 96, 4160)])
+def test_tq_matmul_ws_shapes(dmm, M, N, K):
+    """The prefill shapes with a workspace, one and two planes, activations
+    fp16 cannot hold (one whole row among them)."""
+    tq_ws_case(dmm, M, N, K, 1, torch.float32, seed=M + 11 * N + K)
+    tq_ws_case(dmm, M, N, K, 2, torch.bfloat16, seed=M + 13 * N + K, x_special=True)
+
+
+def test_tq_matmul_ws_small_m_and_errors(dmm):
+    """M below the prefill ignores the workspace; a short one is refused."""
+    rng = np.random.default_rng(77)
+    M, N, K = 8, 40, 256
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    xd = dev(bits16(workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))))
+    ws = torch.empty(dmm.tq_prefill_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    y1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    say("tq_matmul_ws M=8")
+    dmm.tq_matmul_ws(xd, dev(c), dev(bits16(s)), N, 64, y1, ws)
+    dmm.tq_matmul(xd, dev(c), dev(bits16(s)), N, 64, y2)
+    assert torch.equal(y1, y2)
+    short = torch.empty(dmm.tq_prefill_workspace_bytes(M, K) - 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(Exception):
+        dmm.tq_matmul_ws(xd, dev(c), dev(bits16(s)), N, 64, y1, short)
+
+
+def test_tq_matmul_ws_prefill_full(dmm):
+    """ternary_gemv weights at M = 2048 with a workspace: bit for bit the
+    in-kernel conversion's result."""
+    d = workloads.ternary_gemv(M=1)
+    c, s = oracle.quantize_pack(d["W"], 64)
+    rng = np.random.default_rng(60)
+    xd = dev(bits16(workloads.bf16_bits(rng.standard_normal((2048, 4096)).astype(np.float32))))
+    ws = torch.empty(dmm.tq_prefill_workspace_bytes(2048, 4096), dtype=torch.uint8, device=DEV)
+    y_ws = torch.empty((2048, 14336), dtype=torch.bfloat16, device=DEV)
+    y_no = torch.empty((2048, 14336), dtype=torch.bfloat16, device=DEV)
+    say("tq_matmul_ws prefill M=2048 N=14336 K=4096")
+    dmm.tq_matmul_ws(xd, dev(c), dev(bits16(s)), 14336, 64, y_ws, ws)
+    dmm.tq_matmul(xd, dev(c), dev(bits16(s)), 14336, 64, y_no)
+    assert torch.equal(y_ws.view(torch.int16), y_no.view(torch.int16))
