@@ -173,6 +173,10 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
 // Streaming form for a few tokens (dense M <= 4, or <= 16 when the codes stay
 // in LDS; grouped experts); false when the call is outside its domain.
 bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
+// A hot-prefix call (two-plane hot launch, one-plane cold launch that writes
+// the invalid-id rows) as one streaming launch; false outside its domain.
+bool launch_tq_rows_hot(const TqMatmulArgs& hot, const TqMatmulArgs& cold, hipStream_t s,
+                        hipError_t* err);
 // MFMA prefill form for many tokens (dense, one plane, G = 64, M >= 128).
 bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
 int tq_max_grouped_pairs();  // largest M * top_k of a grouped call

@@ -164,9 +164,8 @@ __device__ __forceinline__ Chunk chunk_of(const RowsParams& p, int j) {
 // RU: a dense call of more than four tokens whose blocks all have tiles of
 // their own (passes after the first read no codes).
 template <int PL, int SPB, bool GR, bool RU>
-__global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
-    extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+__device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
+                                             unsigned char* lut, unsigned char* dyn) {
     unsigned char* tiles = dyn;                              // 2 tiles
     constexpr int NSB = SPB == 1 ? kNSB : kNSB - 1;          // blocks in flight
     float* red = (float*)(dyn + (p.all_tiles ? NSB : 2) * p.tile_bytes);   // [blocks][kW][64]
@@ -175,7 +174,7 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     const int lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
     if constexpr (GR) {
-        if ((int)blockIdx.x == p.n_items) {
+        if (bid == p.n_items) {
             // slots whose expert id is out of range: NaN rows
             for (int i = 0; i < p.total; ++i) {
                 const int ei = p.ids[i];
@@ -196,7 +195,7 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
     // lengthening the last.  Every wave holds the ids in registers; wave 0
     // counts the tokens of each expert in the partial buffer (idle until the
     // first tile barrier) and ranks them, one ballot per pass count.
-    int el = GR ? (int)blockIdx.x / p.chunks : 0;            // expert within the launch
+    int el = GR ? bid / p.chunks : 0;                        // expert within the launch
     int vid[4] = {-1, -1, -1, -1};
     const bool ids_in_regs = GR && p.total <= 256;
     if constexpr (GR) {
@@ -240,7 +239,7 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
         }
     }
     const int e = GR ? p.e_begin + el : 0;
-    const int64_t r0 = (int64_t)(GR ? (int)blockIdx.x % p.chunks : (int)blockIdx.x) * p.rows_per_wg;
+    const int64_t r0 = (int64_t)(GR ? bid % p.chunks : bid) * p.rows_per_wg;
     const int64_t r1 = min(r0 + (int64_t)p.rows_per_wg, p.N);
     const int64_t rlast = r1 - 1;
     const int nb = (int)((r1 - r0 + 15) >> 4);
@@ -506,6 +505,27 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
   }
 }
 
+template <int PL, int SPB, bool GR, bool RU>
+__global__ void __launch_bounds__(kT, 1) tq_rows_kernel(RowsParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+    tq_rows_body<PL, SPB, GR, RU>(p, (int)blockIdx.x, lut, dyn);
+}
+
+// A hot-prefix call in one launch: workgroups below ph.n_items take the hot
+// experts' two-plane items (heaviest first within them), the rest the cold
+// experts' one-plane items and, last, the rows of invalid ids.  The hardware
+// hands the cold items to CUs as the hot ones finish, so neither part ends
+// in a round of its own.
+template <int SPBH, int SPBC>
+__global__ void __launch_bounds__(kT, 1) tq_rows_hot_kernel(RowsParams ph, RowsParams pc) {
+    __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+    const int b = (int)blockIdx.x;
+    if (b < ph.n_items) tq_rows_body<2, SPBH, true, false>(ph, b, lut, dyn);
+    else tq_rows_body<1, SPBC, true, false>(pc, b - ph.n_items, lut, dyn);
+}
+
 constexpr int kMaxBlocks = 8;
 constexpr int kLdsLimit = 160 * 1024;
 
@@ -530,8 +550,10 @@ int compute_units() {
 // aligned operands, LDS within the limit; dense calls with 1 <= M <= 4 (up to
 // 16 when the range's blocks all have tiles of their own, so passes after the
 // first re-read no codes), or grouped expert calls (any number of tokens per
-// expert, in passes of four).
-bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
+// expert, in passes of four). rows_setup fills the parameters, LDS bytes,
+// slots per block and grid, and is false outside that domain.
+static bool rows_setup(const TqMatmulArgs& a, RowsParams& p, size_t& smem_out, int& spb_out,
+                       int64_t& wgs_out) {
     const bool grouped = a.n_experts > 0;
     if (a.G != 64 || a.M < 1 || a.N < 1) return false;
     const int64_t ng = a.K / 64;
@@ -539,7 +561,6 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
     if (!al16(a.x) || !al16(a.codes[0]) || !al16(a.scales[0])) return false;
     if (a.planes == 2 && (!al16(a.codes[1]) || !al16(a.scales[1]))) return false;
-    RowsParams p;
     p.x = a.x;
     p.K = a.K;
     p.N = a.N;
@@ -596,11 +617,24 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     const int64_t items = grouped ? (int64_t)(a.e_end - a.e_begin) * p.chunks : p.chunks;
     const int64_t wgs = items + ((grouped && a.nan_rows) ? 1 : 0);
     if (wgs >= (1ll << 31)) return false;
+    p.n_items = (int)items;
+    smem_out = smem;
+    spb_out = spb;
+    wgs_out = wgs;
+    return true;
+}
+
+bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
+    RowsParams p;
+    size_t smem;
+    int spb;
+    int64_t wgs;
+    if (!rows_setup(a, p, smem, spb, wgs)) return false;
     if (wgs == 0) {
         *err = hipSuccess;
         return true;
     }
-    p.n_items = (int)items;
+    const bool grouped = a.n_experts > 0;
     const dim3 grid((unsigned)wgs), block(kT);
 #define DMM_ROWS(PL_, SPB_)                                                                \
     do {                                                                                   \
@@ -616,6 +650,24 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
         else DMM_ROWS(2, 2);
     }
 #undef DMM_ROWS
+    *err = hipGetLastError();
+    return true;
+}
+
+bool launch_tq_rows_hot(const TqMatmulArgs& hot, const TqMatmulArgs& cold, hipStream_t s,
+                        hipError_t* err) {
+    if (hot.n_experts < 1 || cold.n_experts < 1) return false;
+    if (hot.planes != 2 || cold.planes != 1 || hot.nan_rows || !cold.nan_rows) return false;
+    RowsParams ph, pc;
+    size_t smh, smc;
+    int spbh, spbc;
+    int64_t wgh, wgc;
+    if (!rows_setup(hot, ph, smh, spbh, wgh) || !rows_setup(cold, pc, smc, spbc, wgc)) return false;
+    if (spbc != 1 || wgh + wgc >= (1ll << 31)) return false;
+    const size_t smem = smh > smc ? smh : smc;
+    const dim3 grid((unsigned)(wgh + wgc)), block(kT);
+    if (spbh == 1) hipLaunchKernelGGL((tq_rows_hot_kernel<1, 1>), grid, block, smem, s, ph, pc);
+    else hipLaunchKernelGGL((tq_rows_hot_kernel<2, 1>), grid, block, smem, s, ph, pc);
     *err = hipGetLastError();
     return true;
 }
