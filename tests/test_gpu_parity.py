@@ -444,6 +444,39 @@ def test_tq_matmul_hot_prefix(dmm, K):
     hot_case(dmm, E, N, K, T, top_k, 2, seed=K + 9, bad_ids=True, ydt=torch.bfloat16)
 
 
+@pytest.mark.parametrize("K", [256, 1024, 4096])
+def test_tq_matmul_hot_equals_plain_grouped(dmm, K):
+    """tq_matmul_hot against the plain grouped calls on the same ids, bit for
+    bit: a (token, slot) of a hot expert equals the two-plane call over all
+    experts, one of a cold expert the one-plane call (same per-row
+    arithmetic; the hot call only changes which workgroups run which
+    experts), and invalid ids are NaN in all three."""
+    rng = np.random.default_rng(70 + K)
+    E, N, T, top_k, n_hot = 6, 40, 9, 3, 2
+    W = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    xb = dev(bits16(workloads.bf16_bits(rng.standard_normal((T, K)).astype(np.float32))))
+    ids = np.stack([rng.choice(E, top_k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[1, 2] = -1
+    ids[T - 1, 0] = E + 3
+    (c1, s1), (c2, s2) = oracle.two_plane(W, 64)
+    c1d, s1d, idd = dev(c1), dev(bits16(s1)), dev(ids)
+    yh, y2, y1 = (torch.empty((T, top_k, N), dtype=torch.float32, device=DEV) for _ in range(3))
+    say(f"tq_matmul_hot vs plain grouped K={K}")
+    dmm.tq_matmul_hot(xb, c1d, s1d, N, 64, yh, n_hot, E, idd, top_k,
+                      dev(c2[:n_hot * N]), dev(bits16(s2[:n_hot * N])))
+    dmm.tq_matmul(xb, c1d, s1d, N, 64, y2, dev(c2), dev(bits16(s2)), n_experts=E,
+                  expert_ids=idd, top_k=top_k)
+    dmm.tq_matmul(xb, c1d, s1d, N, 64, y1, n_experts=E, expert_ids=idd, top_k=top_k)
+    h, a2, a1 = host(yh), host(y2), host(y1)
+    valid = (ids >= 0) & (ids < E)
+    hot = valid & (ids < n_hot)
+    cold = valid & (ids >= n_hot)
+    assert hot.any() and cold.any()
+    assert np.array_equal(h[hot], a2[hot])
+    assert np.array_equal(h[cold], a1[cold])
+    assert np.all(np.isnan(h[~valid])) and np.all(np.isnan(a2[~valid]))
+
+
 def test_tq_grouped_equals_dense_when_one_expert(dmm):
     """Every (token, slot) routed to expert 2 gives, slot by slot, exactly the
     dense result of expert 2's package (same kernel arithmetic)."""
