@@ -159,29 +159,62 @@ def blas_threads():
         return 1
 
 
+def host_cpu():
+    """(cores this process may run on, CPU model name from /proc/cpuinfo)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
 def cpu_baseline_routeb(d, M, seconds):
     """The oracle itself on the headline workload: float64 decode of the whole
-    8192 x 8192 code matrix and the float64 matmul with M tokens, repeated
-    until `seconds` have passed."""
+    8192 x 8192 code matrix (numpy indexing, one thread) and the float64
+    matmul with M tokens (numpy's BLAS, its own thread pool), repeated until
+    `seconds` have passed.  Each step is timed on its own."""
     import oracle
     table = oracle.rb_table(d["ladder"])
     reps = 0
+    t_dec = t_mm = 0.0
     t0 = time.perf_counter()
     while True:
+        a = time.perf_counter()
         w = oracle.rb_weights(d["codes"], table, d["alpha"])
+        b = time.perf_counter()
         oracle.matmul_ref(d["x"][:M], w)
+        c = time.perf_counter()
+        t_dec += b - a
+        t_mm += c - b
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
             break
     code_bytes = d["codes"].nbytes * reps
+    host_cores, model = host_cpu()
+    mm_threads = blas_threads()
     return {
         "value": round(code_bytes / el / 1e9, 4),
         "unit": "GB/s",
-        "cores": blas_threads(),
+        # threads the oracle actually ran on (the matmul's BLAS pool; the
+        # decode step is single-threaded)
+        "cores": mm_threads,
         "kind": "oracle",
         "sample": f"{reps} full passes of the float64 oracle (decode 8192x8192 codes, "
                   f"matmul at M={M}) in {el:.1f} s",
+        "host_cores": host_cores,
+        "cpu_model": model,
+        "threads_per_step": {"decode": 1, "matmul": mm_threads},
+        "seconds_per_step": {"decode": round(t_dec / reps, 4), "matmul": round(t_mm / reps, 4)},
     }
 
 

@@ -109,7 +109,7 @@ static int tq_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
     if (M == 0 || N == 0) return TQ_OK;
     if (!y || (K > 0 && (!x || !codes1 || !scales1))) return TQ_ERR_NULL;
     if (n_experts > 0 && !expert_ids) return TQ_ERR_NULL;
-    if (!aligned(x, 4) || !aligned(scales1, 2) || (scales2 && !aligned(scales2, 2)) ||
+    if (!aligned(x, 2) || !aligned(scales1, 2) || (scales2 && !aligned(scales2, 2)) ||
         !aligned(y, y_dtype == TQ_F32 ? 4 : 2) || (expert_ids && !aligned(expert_ids, 4)))
         return TQ_ERR_ALIGN;
     const int64_t row_blocks = (N + 15) / 16;

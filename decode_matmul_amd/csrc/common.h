@@ -16,6 +16,9 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 // 16-byte vectors loaded from 4-byte aligned addresses.
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+// 16-byte vectors of activations at any element offset (2-byte aligned): the
+// hardware serves unaligned global loads, so this is still one dwordx4 load.
+typedef uint32_t u32x4h __attribute__((ext_vector_type(4), aligned(2)));
 
 // ------------------------------------------------------------ conversions
 

@@ -24,7 +24,8 @@
 //    group, as the format requires) at no extra MFMA cost for M <= 4.  More
 //    tokens run further token quads over the same decoded operands.
 //  * Activations are read straight from global memory (they are tiny and
-//    stay in L1/L2); codes stream from HBM once per token chunk of 16.
+//    stay in L1/L2) at any element offset; codes stream from HBM once per
+//    token chunk of 16.
 #include "common.h"
 
 namespace dmm {
@@ -243,7 +244,7 @@ tq_gemv_kernel(Params p) {
                 if (t < ntok) {
                     const int sl = p.grouped ? list[tok0 + t] : (tok0 + t);
                     const int64_t row = p.grouped ? (int64_t)(sl / p.top_k) : (int64_t)sl;
-                    u32x4a w = *(const u32x4a*)(p.x + row * p.K + 8 * c);
+                    u32x4h w = *(const u32x4h*)(p.x + row * p.K + 8 * c);
                     v = u32x4{w.x, w.y, w.z, w.w};
                 }
                 *(u32x4*)(xs + t * p.K + 8 * c) = v;
@@ -286,7 +287,7 @@ tq_gemv_kernel(Params p) {
                             if constexpr (XLDS) {
                                 A = *(const u32x4*)(xs + tl * p.K + (int64_t)g * G + 8 * q);
                             } else {
-                                u32x4a v = *(const u32x4a*)(p.x + xrow * p.K + (int64_t)g * G +
+                                u32x4h v = *(const u32x4h*)(p.x + xrow * p.K + (int64_t)g * G +
                                                             8 * q);
                                 A = u32x4{v.x, v.y, v.z, v.w};
                             }

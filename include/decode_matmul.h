@@ -117,7 +117,8 @@ int tq_unpack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_
  * requirements": second-plane outputs are summed with the first, and the
  * expert matmul selects each token's experts).
  *
- *  x          device bf16 [M, K] (M tokens), 4-byte aligned.
+ *  x          device bf16 [M, K] (M tokens), 2-byte aligned: any element
+ *             offset is accepted (the fastest forms need 16-byte aligned rows).
  *  codes1, scales1   plane 1.  Dense: one [N, K] package.  Grouped:
  *             n_experts packages back to back, [n_experts][N][K/G][...].
  *  codes2, scales2   optional plane 2 with the same layout (NULL = 1 plane);

@@ -149,21 +149,6 @@ def test_pack_full_ternary_gemv(dmm):
     assert st == 0 and np.array_equal(got[0], c) and np.array_equal(got[1], s)
 
 
-def test_pack_full_moe_two_plane_sampled(dmm):
-    """All 64 experts (2 GiB of fp32) packed in one call; two planes checked
-    bit-exact on four sampled experts."""
-    d = workloads.moe_two_plane()
-    W = d["W"].reshape(-1, 4096)
-    say("tq_pack moe_two_plane 131072x4096 two planes")
-    got, st = gpu_pack(dmm, W, 64, 2)
-    assert st == 0
-    for e in (0, 17, 40, 63):
-        rows = slice(e * 2048, (e + 1) * 2048)
-        (c1, s1), (c2, s2) = oracle.two_plane(W[rows], 64)
-        for g, r in zip(got, [c1, s1, c2, s2]):
-            assert np.array_equal(g[rows], r)
-
-
 # ------------------------------------------------------------------ unpack
 
 @pytest.mark.parametrize("rows,K,G", [(256, 256, 64), (11, 70, 64), (7, 300, 128), (1, 64, 64),
@@ -260,18 +245,25 @@ def test_tq_matmul_prefill_shapes(dmm, M, N, K):
 
 def test_tq_matmul_prefill_full(dmm):
     """ternary_gemv weights (14336 x 4096, the oracle's package) at M = 2048
-    tokens: every output against the oracle."""
+    tokens: every output against the oracle, fp32 output (the bound alone)
+    and bf16 output, with and without a workspace."""
     d = workloads.ternary_gemv(M=1)
     c, s = oracle.quantize_pack(d["W"], 64)
     rng = np.random.default_rng(60)
     xb = workloads.bf16_bits(rng.standard_normal((2048, 4096)).astype(np.float32))
-    y = torch.empty((2048, 14336), dtype=torch.bfloat16, device=DEV)
-    say("tq_matmul prefill M=2048 N=14336 K=4096")
-    dmm.tq_matmul(dev(bits16(xb)), dev(c), dev(bits16(s)), 14336, 64, y)
-    got = y_host(y)
     w = oracle.ternary_weights(4096, 64, c, s)
     y_ref, B = oracle.matmul_ref(xb, w)
-    assert_bound(got, y_ref, B, "ternary prefill", "bf16")
+    xd, cd, sd = dev(bits16(xb)), dev(c), dev(bits16(s))
+    for ydt in (torch.float32, torch.bfloat16):
+        y = torch.empty((2048, 14336), dtype=ydt, device=DEV)
+        say(f"tq_matmul prefill M=2048 N=14336 K=4096 {ydt}")
+        dmm.tq_matmul(xd, cd, sd, 14336, 64, y)
+        assert_bound(y_host(y), y_ref, B, f"ternary prefill {ydt}", stored_of(y))
+    ws = torch.empty(dmm.tq_prefill_workspace_bytes(2048, 4096), dtype=torch.uint8, device=DEV)
+    y = torch.empty((2048, 14336), dtype=torch.float32, device=DEV)
+    say("tq_matmul_ws prefill M=2048 fp32")
+    dmm.tq_matmul_ws(xd, cd, sd, 14336, 64, y, ws)
+    assert_bound(y_host(y), y_ref, B, "ternary prefill ws fp32", "f32")
 
 
 TQ_CASES = [
@@ -308,11 +300,14 @@ def test_tq_matmul_streaming_shapes(dmm, M, N, K, planes):
         tq_case(dmm, M, N, K, 64, planes, ydt, seed=7 * M + N + K)
 
 
-@pytest.mark.parametrize("code_off,x_off", [(1, 0), (2, 2), (3, 4), (5, 6)])
+@pytest.mark.parametrize("code_off,x_off", [(1, 0), (2, 2), (3, 4), (5, 6), (0, 1), (7, 3)])
 def test_tq_matmul_offset_views(dmm, code_off, x_off):
-    """Non-zero view offsets of codes (any byte) and x (any 4-byte step)."""
+    """Non-zero view offsets of codes (any byte) and x (any element, odd ones
+    included: a 2-byte aligned x is accepted)."""
     tq_case(dmm, 3, 50, 320, 64, 2, torch.float32, seed=77, code_off=code_off, x_off=x_off)
     tq_case(dmm, 1, 50, 256, 128, 1, torch.float32, seed=78, code_off=code_off, x_off=x_off)
+    tq_case(dmm, 4, 64, 1024, 64, 1, torch.bfloat16, seed=79, code_off=code_off, x_off=x_off)
+    tq_case(dmm, 130, 40, 192, 64, 1, torch.float32, seed=80, code_off=code_off, x_off=x_off)
 
 
 def test_tq_matmul_ternary_gemv_full(dmm):
@@ -497,27 +492,76 @@ def test_tq_grouped_equals_dense_when_one_expert(dmm):
     assert np.array_equal(g[:, 0], d) and np.array_equal(g[:, 1], d)
 
 
-def test_tq_matmul_moe_full_sampled(dmm):
-    """moe_two_plane: 64 experts of 2048 x 4096, 16 tokens, top-8, two planes
-    packed on the GPU; every (token, slot) of eight sampled experts checked."""
+@pytest.fixture(scope="module")
+def moe_workload():
+    """moe_two_plane (64 experts of 2048 x 4096, 16 tokens, top-8) with the
+    oracle's own two planes of every touched expert and the float64
+    reference of every (token, slot): two planes, and plane 1 alone (the
+    cold experts of a hot prefix).  Experts are independent, so the oracle
+    runs them in a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
     d = workloads.moe_two_plane()
     W, x, ids = d["W"], d["x"], d["ids"]
+    experts = sorted(set(ids.reshape(-1).tolist()))
+
+    def one(e):
+        (c1, s1), (c2, s2) = oracle.two_plane(W[e], 64)
+        if e not in experts:
+            return e, (c1, s1, c2, s2), None, None, None
+        tt, jj = np.nonzero(ids == e)
+        ref2 = oracle.matmul_ref(x[tt], oracle.ternary_weights(4096, 64, c1, s1, c2, s2))
+        ref1 = oracle.matmul_ref(x[tt], oracle.ternary_weights(4096, 64, c1, s1))
+        return e, (c1, s1, c2, s2), (tt, jj), ref2, ref1
+
+    with ThreadPoolExecutor(8) as ex:
+        per = {r[0]: r[1:] for r in ex.map(one, range(64))}
+    return d, experts, per
+
+
+def moe_check(got, ids, per, which, what, stored):
+    """Every (token, slot) of every touched expert against its reference
+    (which: 'two' for two planes, or a set of hot experts)."""
+    seen = np.zeros(ids.shape, bool)
+    for e, (_, where, ref2, ref1) in per.items():
+        if where is None:
+            continue
+        tt, jj = where
+        y_ref, B = ref2 if (which == "two" or e in which) else ref1
+        assert_bound(got[tt, jj], y_ref, B, f"{what} expert {e}", stored)
+        seen[tt, jj] = True
+    assert seen.all()
+
+
+def test_tq_matmul_moe_every_expert(dmm, moe_workload):
+    """moe_two_plane at full size: the device pack of all 64 experts (2 GiB of
+    fp32 in one call) matches the oracle's planes bit for bit, and the
+    grouped two-plane matmul and
+    the hot-prefix call (16 hot experts) are checked against the oracle on
+    every (token, slot) of every touched expert, the multi-pass experts
+    (more than four tokens) included, with fp32 and bf16 outputs."""
+    d, experts, per = moe_workload
+    W, x, ids = d["W"], d["x"], d["ids"]
+    counts = np.bincount(ids.reshape(-1), minlength=64)
+    assert len(experts) == 54 and int(counts.max()) > 4
     (c1, s1, c2, s2), st = gpu_pack(dmm, W.reshape(-1, 4096), 64, 2)
     assert st == 0
+    for e, (planes, _, _, _) in per.items():
+        rows = slice(e * 2048, (e + 1) * 2048)
+        for g, r in zip((c1, s1, c2, s2), planes):
+            assert np.array_equal(g[rows], r), f"pack differs on expert {e}"
+    xd, idd = dev(bits16(x)), dev(ids)
+    c1d, s1d, c2d, s2d = dev(c1), dev(bits16(s1)), dev(c2), dev(bits16(s2))
+    for ydt in (torch.float32, torch.bfloat16):
+        y = torch.empty((16, 8, 2048), dtype=ydt, device=DEV)
+        say(f"tq_matmul moe_two_plane every expert {ydt}")
+        dmm.tq_matmul(xd, c1d, s1d, 2048, 64, y, c2d, s2d, n_experts=64, expert_ids=idd, top_k=8)
+        moe_check(y_host(y), ids, per, "two", "moe", stored_of(y))
+    n_hot = 16
     y = torch.empty((16, 8, 2048), dtype=torch.float32, device=DEV)
-    say("tq_matmul moe_two_plane full")
-    dmm.tq_matmul(dev(bits16(x)), dev(c1), dev(bits16(s1)), 2048, 64, y, dev(c2),
-                  dev(bits16(s2)), n_experts=64, expert_ids=dev(ids), top_k=8)
-    got = host(y)
-    experts = sorted(set(ids.reshape(-1).tolist()))
-    sample = experts[:: max(1, len(experts) // 8)][:8]
-    for e in sample:
-        # expected values from the oracle's own two planes of expert e
-        (o1, t1), (o2, t2) = oracle.two_plane(W[e], 64)
-        w = oracle.ternary_weights(4096, 64, o1, t1, o2, t2)
-        tt, jj = np.nonzero(ids == e)
-        y_ref, B = oracle.matmul_ref(x[tt], w)
-        assert_bound(got[tt, jj], y_ref, B, f"moe expert {e}")
+    say("tq_matmul_hot moe_two_plane n_hot=16 every expert")
+    dmm.tq_matmul_hot(xd, c1d, s1d, 2048, 64, y, n_hot, 64, idd, 8,
+                      c2d[:n_hot * 2048], s2d[:n_hot * 2048])
+    moe_check(y_host(y), ids, per, set(range(n_hot)), "moe hot", "f32")
 
 
 # ------------------------------------------------------------------ rb_matmul
@@ -665,17 +709,23 @@ def test_rb_matmul_routeb_gemv_full(dmm):
 
 def test_rb_matmul_routeb_prefill_full(dmm):
     """routeb_prefill: M = 2048, K = N = 8192 with row scales; every output
-    against the oracle."""
+    against the oracle, fp32 output (the bound alone) and bf16 output, with
+    and without a workspace."""
     d = workloads.routeb_prefill()
     table = dmm.rb_table(d["ladder"])
-    y = torch.empty((2048, 8192), dtype=torch.bfloat16, device=DEV)
-    say("rb_matmul routeb_prefill M=2048")
-    dmm.rb_matmul(dev(bits16(d["x"])), dev(d["codes"]), dev(table), d["alpha"], y,
-                  dev(bits16(d["row_scale"])))
-    got = y_host(y)
     w = oracle.rb_weights(d["codes"], oracle.rb_table(d["ladder"]), d["alpha"], d["row_scale"])
     y_ref, B = oracle.matmul_ref(d["x"], w)
-    assert_bound(got, y_ref, B, "routeb_prefill", "bf16")
+    xd, cd, td, rsd = dev(bits16(d["x"])), dev(d["codes"]), dev(table), dev(bits16(d["row_scale"]))
+    for ydt in (torch.float32, torch.bfloat16):
+        y = torch.empty((2048, 8192), dtype=ydt, device=DEV)
+        say(f"rb_matmul routeb_prefill M=2048 {ydt}")
+        dmm.rb_matmul(xd, cd, td, d["alpha"], y, rsd)
+        assert_bound(y_host(y), y_ref, B, f"routeb_prefill {ydt}", stored_of(y))
+    ws = torch.empty(dmm.rb_prefill_workspace_bytes(2048, 8192), dtype=torch.uint8, device=DEV)
+    y = torch.empty((2048, 8192), dtype=torch.float32, device=DEV)
+    say("rb_matmul_ws routeb_prefill M=2048 fp32")
+    dmm.rb_matmul_ws(xd, cd, td, 0, float(d["alpha"]), y, ws, rsd)
+    assert_bound(y_host(y), y_ref, B, "routeb_prefill ws fp32", "f32")
 
 
 # ------------------------------------------------------------------ misc
@@ -705,26 +755,69 @@ def test_zero_sizes_and_empty_k(dmm):
 
 
 def test_bit_determinism(dmm):
-    """Two runs of every matmul kernel give identical bits (fixed-order
-    reductions, no atomics on the accumulation path)."""
+    """Two runs of every kernel family give identical bits (fixed-order
+    reductions, no atomics on the accumulation path): dense ternary GEMV
+    (streaming and general forms), grouped two-plane experts, the hot
+    prefix, the ternary prefill (with and without a workspace), the Route B
+    GEMV and prefill, per-block code books, 7-bit indices, the packer and
+    the encoder."""
     rng = np.random.default_rng(99)
     W = (rng.standard_normal((300, 1024)) * 0.02).astype(np.float32)
     c, s = oracle.quantize_pack(W, 64)
-    xb = dev(bits16(workloads.bf16_bits(rng.standard_normal((40, 1024)).astype(np.float32))))
-    codes = dev(rng.integers(0, 243, (300, 1024), dtype=np.uint8))
+    E, NE = 6, 64
+    WE = (rng.standard_normal((E * NE, 1024)) * 0.02).astype(np.float32)
+    (e1, f1), (e2, f2) = oracle.two_plane(WE, 64)
+    ids = np.stack([rng.choice(E, 3, replace=False) for _ in range(9)]).astype(np.int32)
+    xb = dev(bits16(workloads.bf16_bits(rng.standard_normal((200, 1024)).astype(np.float32))))
+    codes_np = rng.integers(0, 243, (300, 1024), dtype=np.uint8)
+    codes = dev(codes_np)
     tbl = dev(oracle.rb_table(np.array([1, .3, .1, .03, .01], np.float32)))
+    tables = dev(np.stack([oracle.rb_table(np.array([1, .3, .1, .03, .01], np.float32) * (1 + i / 10))
+                           for i in range(10)]))
+    used_np = np.zeros(128, np.uint8)
+    used_np[:100] = np.arange(100, dtype=np.uint8) * 2
+    used_np[100:] = 121
+    small = rng.integers(0, 128, (300, 1024)).astype(np.uint8)
+    c7 = dev(oracle.pack7(small))
+    used = dev(used_np)
+    Wd = dev(W)
     say("determinism")
     outs = []
     for _ in range(2):
-        y1 = torch.empty((4, 300), dtype=torch.float32, device=DEV)
-        dmm.tq_matmul(xb[:4], dev(c), dev(bits16(s)), 300, 64, y1)
-        y2 = torch.empty((4, 300), dtype=torch.float32, device=DEV)
-        dmm.rb_matmul(xb[:4], codes, tbl, 0.02, y2)
-        y3 = torch.empty((40, 300), dtype=torch.float32, device=DEV)
-        dmm.rb_matmul(xb, codes, tbl, 0.02, y3)
-        outs.append([host(t).view(np.uint32) for t in (y1, y2, y3)])
-    for a, b in zip(*outs):
-        assert np.array_equal(a, b)
+        got = []
+
+        def f32(*shape):
+            t = torch.empty(shape, dtype=torch.float32, device=DEV)
+            got.append(t)
+            return t
+        dmm.tq_matmul(xb[:4], dev(c), dev(bits16(s)), 300, 64, f32(4, 300))
+        dmm.tq_matmul(xb[:9], dev(c), dev(bits16(s)), 300, 64, f32(9, 300))
+        dmm.tq_matmul(xb[:9], dev(e1), dev(bits16(f1)), NE, 64, f32(9, 3, NE), dev(e2),
+                      dev(bits16(f2)), n_experts=E, expert_ids=dev(ids), top_k=3)
+        dmm.tq_matmul_hot(xb[:9], dev(e1), dev(bits16(f1)), NE, 64, f32(9, 3, NE), 2, E,
+                          dev(ids), 3, dev(e2[:2 * NE]), dev(bits16(f2[:2 * NE])))
+        dmm.tq_matmul(xb[:200], dev(c), dev(bits16(s)), 300, 64, f32(200, 300))
+        ws = torch.empty(dmm.tq_prefill_workspace_bytes(200, 1024), dtype=torch.uint8, device=DEV)
+        dmm.tq_matmul_ws(xb[:200], dev(c), dev(bits16(s)), 300, 64, f32(200, 300), ws)
+        dmm.rb_matmul(xb[:4], codes, tbl, 0.02, f32(4, 300))
+        dmm.rb_matmul(xb[:40], codes, tbl, 0.02, f32(40, 300))
+        dmm.rb_matmul_blocks(xb[:4], codes, tables, 32, 0.02, f32(4, 300))
+        dmm.rb_matmul_blocks(xb[:40], codes, tables, 32, 0.02, f32(40, 300))
+        dmm.rb_matmul7(xb[:4], c7, 1024, used, tbl, 0, 0.02, f32(4, 300))
+        dmm.rb_matmul7(xb[:40], c7, 1024, used, tbl, 0, 0.02, f32(40, 300))
+        cs, ss = dmm.packed_shape(300, 1024, 64)
+        pc = torch.empty(cs, dtype=torch.uint8, device=DEV)
+        ps = torch.empty(ss, dtype=torch.int16, device=DEV)
+        dmm.tq_pack(Wd, 64, 1, pc, ps)
+        got += [pc, ps]
+        ec = torch.empty((300, 1024), dtype=torch.uint8, device=DEV)
+        ea = torch.empty(301, dtype=torch.float32, device=DEV)
+        er = torch.empty(300, dtype=torch.float16, device=DEV)
+        dmm.rb_encode(Wd, np.array([1, .3, .1, .03, .01], np.float32), ec, ea, row_scale=er)
+        got += [ec, ea, er]
+        outs.append([host(t).view(np.uint8) for t in got])
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert np.array_equal(a, b), f"output {i} differs between two runs"
 
 
 # ------------------------------------------------------------------ rb_encode
@@ -898,6 +991,13 @@ def test_rb_encode_large(dmm):
     W = encode_inputs(4096, 4096, seed=41)
     encode_case(dmm, W, S_LADDER, per_row=True)
     encode_case(dmm, W, S0_LADDER, per_row=False)
+
+
+def test_rb_encode_routeb_encode_full(dmm):
+    """routeb_encode at full size (8192 x 8192 with per-row scales, the timed
+    encoder workload): codes, alpha, the row maxima and rho bit for bit."""
+    d = workloads.routeb_encode()
+    encode_case(dmm, d["W"], d["ladder"], per_row=True)
 
 
 # ----------------------------------------------- prefill with a workspace
