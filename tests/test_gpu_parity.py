@@ -803,8 +803,8 @@ def test_bit_determinism(dmm):
         dmm.rb_matmul(xb[:40], codes, tbl, 0.02, f32(40, 300))
         dmm.rb_matmul_blocks(xb[:4], codes, tables, 32, 0.02, f32(4, 300))
         dmm.rb_matmul_blocks(xb[:40], codes, tables, 32, 0.02, f32(40, 300))
-        dmm.rb_matmul7(xb[:4], c7, 1024, used, tbl, 0, 0.02, f32(4, 300))
-        dmm.rb_matmul7(xb[:40], c7, 1024, used, tbl, 0, 0.02, f32(40, 300))
+        dmm.rb_matmul7(xb[:4], c7, 300, used, tbl, 0, 0.02, f32(4, 300))
+        dmm.rb_matmul7(xb[:40], c7, 300, used, tbl, 0, 0.02, f32(40, 300))
         cs, ss = dmm.packed_shape(300, 1024, 64)
         pc = torch.empty(cs, dtype=torch.uint8, device=DEV)
         ps = torch.empty(ss, dtype=torch.int16, device=DEV)
