@@ -30,7 +30,7 @@ TQ_DATA_ALPHABET = 8
 EXPORTS = ("tq_pack", "tq_unpack", "tq_matmul", "tq_matmul_hot", "rb_table", "rb_encode",
            "rb_matmul", "rb_matmul_rho_block", "rb_matmul_blocks", "rb_truncate",
            "rb_matmul7", "rb_matmul_ws", "rb_prefill_workspace_bytes", "tq_matmul_ws",
-           "tq_prefill_workspace_bytes", "tq_status_string")
+           "tq_prefill_workspace_bytes", "rb_matmul_noalloc", "tq_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -63,6 +63,8 @@ _lib.rb_matmul_ws.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i32, ctypes.c_float
                               _p, _p, _i32, _p, _i64, _p]
 _lib.rb_prefill_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tq_matmul_ws.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _i64, _i32, _p, _i32, _p, _i64, _p]
+_lib.rb_matmul_noalloc.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i32, ctypes.c_float, _p, _i32,
+                                   _p, _p, _i32, _p]
 _lib.tq_prefill_workspace_bytes.argtypes = [_i64, _i64]
 _lib.tq_status_string.argtypes = [_i32]
 _lib.tq_status_string.restype = ctypes.c_char_p
@@ -363,6 +365,28 @@ def rb_matmul_ws(x, codes, tables, table_rows, alpha, y, workspace, row_scale=No
                            float(alpha), _ptr(row_scale), int(rho_rows), _ptr(bias), _ptr(y),
                            _ydtype(y), _ptr(workspace), nbytes, _stream(dev))
     _raise(rc, "rb_matmul_ws")
+
+
+def rb_matmul_noalloc(x, codes, tables, table_rows, alpha, y, row_scale=None, bias=None,
+                      rho_rows=1):
+    """rb_matmul_ws whose workspace is the library's own per-device scratch
+    array (DMM_SCRATCH_BYTES): the call allocates nothing."""
+    dev = x.device
+    M, K = x.shape
+    N = codes.shape[0]
+    _need(x, "x", _BF16, M * K, dev)
+    _need(codes, "codes", _U8, N * K, dev)
+    _tables(tables, N, table_rows, dev)
+    if row_scale is not None:
+        _need(row_scale, "row_scale", _H16, -(-N // int(rho_rows)) if rho_rows > 0 else N, dev)
+    if bias is not None:
+        _need(bias, "bias", _F32, N, dev)
+    _need(y, "y", (y.dtype,), M * N, dev)
+    with torch.cuda.device(dev):
+        rc = _lib.rb_matmul_noalloc(_ptr(x), M, K, _ptr(codes), N, _ptr(tables), int(table_rows),
+                                    float(alpha), _ptr(row_scale), int(rho_rows), _ptr(bias),
+                                    _ptr(y), _ydtype(y), _stream(dev))
+    _raise(rc, "rb_matmul_noalloc")
 
 
 def rb7_row_bytes(K):

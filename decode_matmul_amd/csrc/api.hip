@@ -27,6 +27,8 @@ const char* tq_status_string(int status) {
         case TQ_ERR_DTYPE: return "unknown dtype";
         case TQ_ERR_ALIGN: return "a pointer is not aligned as documented";
         case TQ_ERR_HIP: return "the HIP runtime rejected a launch";
+        case TQ_ERR_SCRATCH:
+            return "the call needs more device scratch than DMM_SCRATCH_BYTES (34 MiB)";
         default: return "unknown status";
     }
 }
@@ -226,7 +228,8 @@ static int rb_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
                             const uint8_t* used, int64_t N, const float* table,
                             int32_t table_rows, float alpha, const uint16_t* row_scale,
                             int32_t rho_rows, const float* bias, void* y, int32_t y_dtype,
-                            void* stream, void* workspace = nullptr, int64_t workspace_bytes = 0) {
+                            void* stream, void* workspace = nullptr, int64_t workspace_bytes = 0,
+                            bool static_scratch = false) {
     if (M < 0 || K < 0 || N < 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
         return TQ_ERR_SHAPE;
     if (rho_rows < 1 || table_rows < 0) return TQ_ERR_SHAPE;
@@ -259,6 +262,12 @@ static int rb_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
         return hip_status(used ? dmm::launch_rb7_gemv(a, s) : dmm::launch_rb_gemv(a, s));
     }
     if ((M + 255) / 256 >= 65536) return TQ_ERR_SHAPE;
+    if (static_scratch) {
+        // the library's own per-device array stands in for the workspace
+        if (dmm::rb_prefill_ws_bytes(M, K) > dmm::kScratchBytes) return TQ_ERR_SCRATCH;
+        if (dmm::scratch_of_current_device(&workspace) != hipSuccess) return TQ_ERR_HIP;
+        workspace_bytes = dmm::kScratchBytes;
+    }
     if (workspace) {
         if (!aligned(workspace, 256)) return TQ_ERR_ALIGN;
         if (workspace_bytes < dmm::rb_prefill_ws_bytes(M, K)) return TQ_ERR_SHAPE;
@@ -278,6 +287,14 @@ int rb_matmul_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, 
                  int64_t workspace_bytes, void* stream) {
     return rb_matmul_common(x, M, K, codes, nullptr, N, tables, table_rows, alpha, row_scale,
                             rho_rows, bias, y, y_dtype, stream, workspace, workspace_bytes);
+}
+
+int rb_matmul_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                      const float* tables, int32_t table_rows, float alpha,
+                      const uint16_t* row_scale, int32_t rho_rows, const float* bias, void* y,
+                      int32_t y_dtype, void* stream) {
+    return rb_matmul_common(x, M, K, codes, nullptr, N, tables, table_rows, alpha, row_scale,
+                            rho_rows, bias, y, y_dtype, stream, nullptr, 0, true);
 }
 
 int rb_matmul_rho_block(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,

@@ -208,6 +208,13 @@ inline int64_t rb_prefill_ws_bytes(int64_t M, int64_t K) {
     return rb_prefill_ws_flags_offset(M, K) + (M + 255) / 256 * ((K + 31) / 32) * 4;
 }
 
+// Library-owned scratch of rb_matmul_noalloc: one array per device, as large
+// as the prefill workspace of M = 2048 tokens at K = 8192 plus room to spare.
+constexpr int64_t kScratchBytes = DMM_SCRATCH_BYTES;
+// Device address of the scratch array on the current device (looked up once
+// per device, then cached).
+hipError_t scratch_of_current_device(void** out);
+
 // Bytes of one row of 7-bit indices.
 inline int64_t rb7_row_bytes(int64_t K) { return (7 * K + 7) / 8; }
 

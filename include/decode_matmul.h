@@ -56,8 +56,14 @@ enum tq_status {
     TQ_ERR_UNSUPPORTED = 3,  /* G not in {64, 128}, planes not in {1, 2}, ...   */
     TQ_ERR_DTYPE = 4,        /* unknown output dtype                           */
     TQ_ERR_ALIGN = 5,        /* a pointer is not aligned as documented         */
-    TQ_ERR_HIP = 6           /* the HIP runtime rejected a launch              */
+    TQ_ERR_HIP = 6,          /* the HIP runtime rejected a launch              */
+    TQ_ERR_SCRATCH = 7       /* the call needs more than the library's static
+                                scratch (DMM_SCRATCH_BYTES) holds               */
 };
+
+/* Bytes of the device scratch array that rb_matmul_noalloc uses in place of a
+   workspace; each GPU the library runs on holds one until the process ends. */
+#define DMM_SCRATCH_BYTES ((int64_t)34 << 20)
 
 /* Device-side data-error flags, OR-ed into *d_status. */
 enum tq_data_flag {
@@ -363,6 +369,32 @@ int rb_matmul_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, 
                  const float* tables, int32_t table_rows, float alpha, const uint16_t* row_scale,
                  int32_t rho_rows, const float* bias, void* y, int32_t y_dtype, void* workspace,
                  int64_t workspace_bytes, void* stream);
+
+/*
+ * rb_matmul_noalloc -- rb_matmul_ws for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the workspace is the library's own static device array
+ * of DMM_SCRATCH_BYTES, one per GPU, instead of caller memory.
+ *
+ * Arguments, computation, accuracy and output are those of rb_matmul_ws
+ * without its workspace arguments; the output is bit for bit that of
+ * rb_matmul_ws.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *
+ *  - M > 16 with rb_prefill_workspace_bytes(M, K) > DMM_SCRATCH_BYTES gives
+ *    TQ_ERR_SCRATCH before any launch (M = 2048 at K = 8192 fits).
+ *  - The scratch of the calling thread's current device is used: `stream`
+ *    must belong to that device.
+ *  - Every call on a GPU shares that GPU's array and overwrites it; calls
+ *    that overlap in time on one GPU (two streams, two threads) race.
+ *    The array's contents on entry do not matter.
+ *  - The array's device address is looked up on the first call on each
+ *    device; TQ_ERR_HIP if the lookup fails.
+ */
+int rb_matmul_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                      const float* tables, int32_t table_rows, float alpha,
+                      const uint16_t* row_scale, int32_t rho_rows, const float* bias, void* y,
+                      int32_t y_dtype, void* stream);
 
 /*
  * rb_truncate -- the 7-bit truncated alphabet (Route B paper, section 8.1: a

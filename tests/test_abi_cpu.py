@@ -19,6 +19,7 @@ dmm = pytest.importorskip("decode_matmul_amd")
 lib = dmm.raw()
 
 TQ_ERR_NULL, TQ_ERR_SHAPE, TQ_ERR_UNSUPPORTED, TQ_ERR_DTYPE, TQ_ERR_ALIGN = 1, 2, 3, 4, 5
+TQ_ERR_SCRATCH = 7
 FAKE = ctypes.c_void_p(0x10000)          # never dereferenced: every call below fails first
 FAKE_ODD = ctypes.c_void_p(0x10001)
 
@@ -36,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert lib.tq_status_string(s) and lib.tq_status_string(s) != b"unknown status"
     assert lib.tq_status_string(99) == b"unknown status"
 
@@ -104,6 +105,26 @@ def test_matmul_argument_errors():
     bad = list(ok); bad[1] = 0                         # M = 0: no-op
     assert f(*bad) == 0
     bad = list(ok); bad[7] = 0                         # N = 0: no-op
+    assert f(*bad) == 0
+
+
+def test_rb_matmul_noalloc_argument_errors():
+    """The allocation-free prefill entry point checks its arguments like
+    rb_matmul_ws, and refuses a prefill whose workspace would exceed the
+    library's static scratch before touching a device."""
+    f = lib.rb_matmul_noalloc
+    ok = [FAKE, 2048, 8192, FAKE, 8, FAKE, 0, ctypes.c_float(0.02), None, 1, None, FAKE, 0, None]
+    bad = list(ok); bad[3] = None
+    assert f(*bad) == TQ_ERR_NULL
+    bad = list(ok); bad[12] = 2
+    assert f(*bad) == TQ_ERR_DTYPE
+    bad = list(ok); bad[0] = FAKE_ODD
+    assert f(*bad) == TQ_ERR_ALIGN
+    bad = list(ok); bad[1] = 4096                      # 64 MiB of fp16 activations
+    assert f(*bad) == TQ_ERR_SCRATCH
+    assert dmm.rb_prefill_workspace_bytes(2048, 8192) <= 34 << 20
+    assert dmm.rb_prefill_workspace_bytes(4096, 8192) > 34 << 20
+    bad = list(ok); bad[1] = 0                         # M = 0: no-op
     assert f(*bad) == 0
 
 
