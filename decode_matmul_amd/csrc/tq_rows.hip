@@ -83,29 +83,64 @@ struct RowsParams {
     int64_t e_codes, e_scales;   // bytes per expert in a code / scale plane
 };
 
-// bf16 high bytes of 2t for the five trits of byte b (t = digit - 1, digit q
-// of b in base 3 least significant first): trits 0..3 in .x, trit 4 in .y;
-// bytes 243..255 decode to zero.  Built at compile time.
-struct TritBytes {
-    uint32_t lo[256];
-    uint32_t hi[256];
+// Code book of byte b: trits 0..3 (digit q of b in base 3, least significant
+// first, t = digit - 1) as two ready bf16 pairs (2t0, 2t1) and (2t2, 2t3),
+// each value 2t stored as its high byte (0x40, 0x00 or 0xC0) over a zero low
+// byte.  Trit 4 is computed arithmetically (t4pair).  Bytes 243..255 decode
+// to zero.  Built at compile time.
+constexpr uint32_t trit_hb(int d) { return d == 2 ? 0x40u : (d == 0 ? 0xC0u : 0x00u); }
+struct TritPairs {
+    uint2 e[256];
 };
-constexpr TritBytes make_trit_bytes() {
-    TritBytes t{};
+constexpr TritPairs make_trit_pairs() {
+    TritPairs t{};
     for (int b = 0; b < 243; ++b) {
-        int v = b;
-        uint32_t h[5] = {0, 0, 0, 0, 0};
-        for (int q = 0; q < 5; ++q) {
-            const int d = v % 3;
-            h[q] = d == 2 ? 0x40u : (d == 0 ? 0xC0u : 0x00u);
-            v /= 3;
-        }
-        t.lo[b] = h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24);
-        t.hi[b] = h[4];
+        const int d0 = b % 3, d1 = (b / 3) % 3, d2 = (b / 9) % 3, d3 = (b / 27) % 3;
+        t.e[b].x = (trit_hb(d0) << 8) | (trit_hb(d1) << 24);
+        t.e[b].y = (trit_hb(d2) << 8) | (trit_hb(d3) << 24);
     }
     return t;
 }
-__constant__ TritBytes kTritBytes = make_trit_bytes();
+__constant__ TritPairs kTritPairs = make_trit_pairs();
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Trit 4 (the most significant digit, floor(b / 81)) of two code bytes held
+// in the low bytes of the two 16-bit halves, as a bf16 pair of 2 t4: with
+// v = 203 b + 0xC000 (mod 2^16) bits 14..15 are digit + 3 (mod 4), since
+// floor(203 b / 2^14) = floor(b / 81) for b <= 242, which the masked value
+// reads as 0xC000 (-2), 0 or 0x4000 (+2).
+__device__ __forceinline__ uint32_t t4pair(uint32_t bytes16) {
+    u16x2 v = __builtin_bit_cast(u16x2, bytes16);
+    v = v * (u16x2){203, 203} + (u16x2){0xC000, 0xC000};
+    return __builtin_bit_cast(uint32_t, v) & 0xC000C000u;
+}
+
+// K order of a group inside the MFMA operands.  The 32 B-operand dwords of a
+// lane (four per MFMA, eight MFMAs) are: for bytes i = 0..12 the two code-book
+// pairs (t_5i, t_5i+1), (t_5i+2, t_5i+3) as dwords 2i, 2i+1; then, for the
+// code dwords k = 0..2 (bytes 4k..4k+3), trit 4 of bytes (4k, 4k+2) and of
+// bytes (4k+1, 4k+3) as dwords 26 + 2k and 27 + 2k.  Byte 12's trit 4 is
+// padding and is not used.  The activations are placed in the same order.
+__device__ __forceinline__ void permute_group_x(const uint32_t (&xw)[32], u32x4 (&A)[8]) {
+    uint32_t a[32];
+#pragma unroll
+    for (int d = 0; d < 26; ++d) {
+        const int i = d >> 1, h = d & 1, t = 5 * i + 2 * h;          // first trit of the pair
+        a[d] = (t & 1) ? align_bytes(xw[(t + 1) >> 1], xw[(t - 1) >> 1], 2) : xw[t >> 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        const int k = j >> 1;
+        const int ta = (j & 1) ? 20 * k + 9 : 20 * k + 4;               // trit 4 of byte 4k (+1)
+        const int tb = (j & 1) ? 20 * k + 19 : 20 * k + 14;             // trit 4 of byte 4k+2 (+3)
+        const uint32_t sa = (ta & 1) ? 0x0302u : 0x0100u;
+        const uint32_t sb = (tb & 1) ? 0x0706u : 0x0504u;
+        a[26 + j] = perm_b32(xw[tb >> 1], xw[ta >> 1], sa | (sb << 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) A[j] = u32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+}
 
 // 16-byte chunk j of a block: where it comes from and where it goes.
 struct Chunk {
@@ -286,8 +321,8 @@ __device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
         if (ntok == 0) return;                   // whole workgroup: nothing routed here
     }
     const int npass = (ntok + 3) >> 2;
-    // the trit table entry of this thread, read ahead of every other load
-    const uint32_t tt_lo = kTritBytes.lo[tid >> 2], tt_hi = kTritBytes.hi[tid >> 2];
+    // the code-book entry of this thread, read ahead of every other load
+    const uint2 tt = kTritPairs.e[tid >> 2];
     __builtin_amdgcn_sched_barrier(0);
 
     const int col = lane & 15;
@@ -296,7 +331,7 @@ __device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
     const bool quad_ok = wave < nquads;
     const int g = 4 * wave + kb;
     const int ar = lane & 15;
-    const uint32_t cofs = (uint32_t)col << 3;
+    const uint32_t cofs = (uint32_t)(lane & 31) << 3;    // code-book copy lane % 32
 
     // this thread's chunks of every block: byte offset (from p.base) in block
     // 0, the offset of the same chunk in the last row of the range (rows past
@@ -354,13 +389,16 @@ __device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
     // ---- activations of this wave's quad, block diagonal, zero elsewhere
     // (loaded first so that masking them below waits for these loads only)
     const bool a_ok = (ar & 3) == kb && (ar >> 2) < mt && quad_ok;
-    u32x4 A[8];
+    uint32_t xw[32];
     {
         const int mc = x_row(min(ar >> 2, mt - 1));
         const int gc = quad_ok ? g : 0;
         const uint16_t* xp = p.x + (int64_t)mc * p.K + (int64_t)gc * 64;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) A[q] = *(const u32x4*)(xp + 8 * q);
+        for (int q = 0; q < 8; ++q) {
+            const u32x4 v = *(const u32x4*)(xp + 8 * q);
+            xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
+        }
     }
     __builtin_amdgcn_sched_barrier(0);     // activations are issued before the code stream
 
@@ -372,17 +410,20 @@ __device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
 #pragma unroll
         for (int d = 0; d < NSB; ++d) load(d, R[d]);
 
-    // ---- trit table, 16 copies (first pass; read only after the first barrier)
+    // ---- code book, 32 copies (first pass; read only after the first barrier)
     if (pass == 0) {
-        // entry tid / 4, copies 4 (tid & 3) .. + 3
-        const uint2 e = make_uint2(tt_lo, tt_hi);
-        unsigned char* d = lut + (((tid >> 2) << 8) | ((4 * (tid & 3)) << 3));
+        // entry tid / 4, copies 8 (tid & 3) .. + 7; the four 16-byte stores are
+        // rotated by tid / 4 so that the lanes of each store spread over the banks
+        const u32x4 e = {tt.x, tt.y, tt.x, tt.y};
+        unsigned char* d = lut + (((tid >> 2) << 8) | (64 * (tid & 3)));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *(uint2*)(d + 8 * c) = e;
+        for (int c = 0; c < 4; ++c) *(u32x4*)(d + 16 * ((c + (tid >> 2)) & 3)) = e;
     }
 
+    u32x4 A[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) A[q] = a_ok ? A[q] : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < 32; ++q) xw[q] = a_ok ? xw[q] : 0u;
+    permute_group_x(xw, A);
 
     auto store = [&](int buf, const u32x4 (&R)[SPB]) {
         unsigned char* t = tiles + buf * p.tile_bytes;
@@ -413,49 +454,38 @@ __device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
                 D[1] = align_bytes(W2, W1, sh);
                 D[2] = align_bytes(W3, W2, sh);
                 D[3] = align_bytes(0u, W3, sh);
-                // in two halves (trits 0..31 from bytes 0..6, trits 32..63 from
-                // bytes 6..12), each feeding four MFMAs, to bound the live words
-                uint32_t Elo[kNB], Ehi[kNB];
+                // B operands in the group's K order (see permute_group_x)
+                u32x4 Bq[8];
+#pragma unroll
+                for (int i = 0; i < kNB; ++i) {
+                    const uint32_t a = perm_b32(D[i >> 2], cofs, 0x0c0c0400u + ((uint32_t)(i & 3) << 8));
+                    const uint2 e2 = *(const uint2*)(lut + a);
+                    Bq[i >> 1][2 * (i & 1)] = e2.x;
+                    Bq[i >> 1][2 * (i & 1) + 1] = e2.y;
+                }
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    const int d = 26 + 2 * k;
+                    Bq[d >> 2][d & 3] = t4pair(D[k] & 0x00FF00FFu);
+                    Bq[(d + 1) >> 2][(d + 1) & 3] = t4pair(perm_b32(D[k], D[k], 0x0c030c01u));
+                }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-#pragma unroll
-                    for (int i = half == 0 ? 0 : 7; i < (half == 0 ? 7 : kNB); ++i) {
-                        const uint32_t a = perm_b32(D[i >> 2], cofs, 0x0c0c0400u + ((uint32_t)(i & 3) << 8));
-                        const uint2 e2 = *(const uint2*)(lut + a);
-                        Elo[i] = e2.x;
-                        Ehi[i] = e2.y;
-                    }
-                    uint32_t B[16];
-#pragma unroll
-                    for (int p3 = 0; p3 < 16; ++p3) {
-                        const int p2 = 16 * half + p3;
-                        const int ja = 2 * p2, jb = 2 * p2 + 1;
-                        const int ia = ja / 5, qa = ja % 5, ib = jb / 5, qb = jb % 5;
-                        const uint32_t ra = qa < 4 ? Elo[ia] : Ehi[ia];
-                        const uint32_t rbv = qb < 4 ? Elo[ib] : Ehi[ib];
-                        const uint32_t ba = qa < 4 ? qa : 0, bb = qb < 4 ? qb : 0;
-                        const bool same = (ia == ib) && ((qa < 4) == (qb < 4));
-                        B[p3] = same ? perm_b32(ra, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | (bb << 24))
-                                     : perm_b32(rbv, ra, 0x0cu | (ba << 8) | (0x0cu << 16) | ((4u + bb) << 24));
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const u32x4 bq = {B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]};
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, A[4 * half + q]), __builtin_bit_cast(bf16x8, bq),
-                            acc, 0, 0, 0);
-                    }
-                }
-                // scales of groups 4w .. 4w+3 of row col (C rows 4m + i)
+                for (int j = 0; j < 8; ++j)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, A[j]), __builtin_bit_cast(bf16x8, Bq[j]), acc, 0, 0, 0);
+                // scales of groups 4w .. 4w+3 of row col (C rows 4m + i); the
+                // factor 1/2 of the code book's 2t is applied after the sum
                 const uint2 sw = *(const uint2*)(t + PL * 16 * p.pitch + pl * 16 * p.spitch +
                                                  col * p.spitch + 8 * wave);
-                const float s0 = f16_bits_to_f32((uint16_t)(sw.x & 0xffffu));
-                const float s1 = f16_bits_to_f32((uint16_t)(sw.x >> 16));
-                const float s2 = f16_bits_to_f32((uint16_t)(sw.y & 0xffffu));
-                const float s3 = f16_bits_to_f32((uint16_t)(sw.y >> 16));
-                // the table holds 2t: halve once
-                part += 0.5f * (s0 * acc[0] + s1 * acc[1] + s2 * acc[2] + s3 * acc[3]);
+                const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(sw.x & 0xffffu));
+                const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(sw.x >> 16));
+                const _Float16 h2 = __builtin_bit_cast(_Float16, (uint16_t)(sw.y & 0xffffu));
+                const _Float16 h3 = __builtin_bit_cast(_Float16, (uint16_t)(sw.y >> 16));
+                part = __builtin_fmaf((float)h0, acc[0], part);
+                part = __builtin_fmaf((float)h1, acc[1], part);
+                part = __builtin_fmaf((float)h2, acc[2], part);
+                part = __builtin_fmaf((float)h3, acc[3], part);
             }
         }
         red[(blk * kW + wave) * 64 + lane] = part;
@@ -495,6 +525,7 @@ __device__ __forceinline__ void tq_rows_body(const RowsParams& p, const int bid,
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < kW; ++w) v += red[(blk * kW + w) * 64 + l];
+        v *= 0.5f;                             // the code book holds 2t
         if (m < mt && n < r1) {
             const int64_t idx = (int64_t)out_row(m) * p.N + n;
             if (p.y_dtype == TQ_F32) ((float*)p.y)[idx] = v;
