@@ -160,7 +160,8 @@ static int tq_matmul_common(const uint16_t* x, int64_t M, int64_t K, const uint8
     cold.scales[1] = nullptr;
     cold.e_begin = n_hot;
     hipError_t e = hipSuccess;
-    if (dmm::launch_tq_rows_hot(hot, cold, s, &e)) return hip_status(e);   // one launch
+    if (dmm::launch_tq_wave_hot(hot, cold, s, &e)) return hip_status(e);   // one launch
+    if (dmm::launch_tq_rows_hot(hot, cold, s, &e)) return hip_status(e);
     e = dmm::launch_tq_matmul(hot, s);
     if (e != hipSuccess) return TQ_ERR_HIP;
     return hip_status(dmm::launch_tq_matmul(cold, s));

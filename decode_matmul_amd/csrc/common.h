@@ -176,9 +176,14 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
 // Streaming form for a few tokens (dense M <= 4, or <= 16 when the codes stay
 // in LDS; grouped experts); false when the call is outside its domain.
 bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
-// Wave-local form for dense calls of 1..4 tokens (G = 64, K = 1024..4096 in
-// steps of 1024); false when the call is outside its domain.
+// Wave-local form for dense calls of 1..4 tokens and grouped calls of at
+// most 256 (token, slot) pairs (G = 64, K = 1024..4096 in steps of 1024);
+// false when the call is outside its domain.
 bool launch_tq_wave(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
+// A hot-prefix call (two-plane hot launch, one-plane cold launch that writes
+// the invalid-id rows) as one wave-local launch; false outside its domain.
+bool launch_tq_wave_hot(const TqMatmulArgs& hot, const TqMatmulArgs& cold, hipStream_t s,
+                        hipError_t* err);
 // A hot-prefix call (two-plane hot launch, one-plane cold launch that writes
 // the invalid-id rows) as one streaming launch; false outside its domain.
 bool launch_tq_rows_hot(const TqMatmulArgs& hot, const TqMatmulArgs& cold, hipStream_t s,
