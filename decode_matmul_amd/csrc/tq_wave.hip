@@ -128,6 +128,14 @@ __device__ __forceinline__ void fill_book(unsigned char* lut, int tid) {
 // One launch's work (a dense call, or the experts of one grouped call) on a
 // workgroup: lut is the code book (filled here when book is set), xs the
 // staged activations, meta the grouped bookkeeping, red the per-round slices.
+// Issue priority after a wave's task t of a round (3 at the round's start):
+// a wave that is ahead yields to those behind.
+__device__ __forceinline__ void yield_after(int t) {
+    if (t == 0) __builtin_amdgcn_s_setprio(2);
+    else if (t == 1) __builtin_amdgcn_s_setprio(1);
+    else if (t == 2) __builtin_amdgcn_s_setprio(0);
+}
+
 // A operands of lane (b, j): token j's group g from the staged activations,
 // in the K order above (zero for j >= nt).
 __device__ __forceinline__ void build_a(const unsigned char* xs, int j, int g, int nt, u32x2 (&A)[16]) {
@@ -185,30 +193,49 @@ __device__ __forceinline__ void decode_task(const u32x4 (&c)[PL], const uint16_t
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float v = tot[r];
-        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+        // (a rotation inside the row reads valid lanes only; bound_ctrl lets
+        // the move fold into the add)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
         tot[r] = v;
     }
     if ((lane & 12) == 0) *(f32x4*)(dst + (lane >> 4) * 16 + 4 * (lane & 3)) = tot;
 }
 
 // y[m, n] = 1/2 (the code book holds 2t) of the sum over the slices and the
-// four lane rows of row n, in a fixed order: slices of row quad rq at
-// red + (rq nkq + q) kTaskStride, nrows rows from row n0, y row yrow(m).
+// four lane rows of row n, in a fixed order: the slices of row quad rq sit at
+// red + (rq nkq + q) kTaskStride; nrows rows from row n0, y row yrow(m).
+// Thread (rq, c, q) sums slice q of row 4 rq + c over the lane rows (one
+// float4 per lane row: the four tokens), the four threads of a row add their
+// sums pairwise, and thread q writes token q.
 template <typename YRow>
 __device__ __forceinline__ void write_rows(const float* red, int nkq, int nrows, int nt, int64_t n0,
                                            int64_t N, void* y, int y_dtype, YRow yrow) {
-    for (int o = threadIdx.x; o < nrows * nt; o += kT) {
-        const int m = o / nrows, rloc = o - m * nrows;
-        const int rq = rloc >> 2, c = rloc & 3;
-        float v = 0.f;
-        for (int q = 0; q < nkq; ++q)
+    const int tid = threadIdx.x;
+    const int q = tid & 3, c = (tid >> 2) & 3, rq = tid >> 4;
+    const int row = 4 * rq + c;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row < nrows && q < nkq) {
+        const float* src = red + (rq * nkq + q) * kTaskStride + 4 * c;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v += red[(rq * nkq + q) * kTaskStride + r * 16 + 4 * c + m];
-        v *= 0.5f;
-        const int64_t idx = yrow(m) * N + n0 + rloc;
-        if (y_dtype == TQ_F32) ((float*)y)[idx] = v;
-        else ((uint16_t*)y)[idx] = f32_to_bf16_rne(v);
+        for (int r = 0; r < 4; ++r) {
+            const f32x4 w = *(const f32x4*)(src + 16 * r);
+            v[0] += w[0]; v[1] += w[1]; v[2] += w[2]; v[3] += w[3];
+        }
+    }
+    // (q0 + q1) + (q2 + q3) on every lane of the quad (addition commutes)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        float t = v[m];
+        t += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0xB1, 0xF, 0xF, true));
+        t += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, true));
+        v[m] = t;
+    }
+    if (row < nrows && q < nt) {
+        const float o = 0.5f * (q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3]);
+        const int64_t idx = yrow(q) * N + n0 + row;
+        if (y_dtype == TQ_F32) ((float*)y)[idx] = o;
+        else ((uint16_t*)y)[idx] = f32_to_bf16_rne(o);
     }
 }
 
@@ -251,20 +278,27 @@ __global__ void __launch_bounds__(kT, 1) tq_wave_dense_kernel(WaveParams p) {
     // activations: memory counters retire in order, so waiting for x does
     // not wait for it.  Every task is loaded (past the end: the last row
     // quad again, a cache hit), so that no load sits under a branch.
+    // The row quad's first row is uniform (a scalar base address); a lane
+    // adds its own 32-bit offset.
     u32x4 C[kMaxTasks][PL];
     uint16_t S[kMaxTasks][PL];
+    const uint32_t lane_co = (uint32_t)(kNB * g) - sh, lane_so = 2u * (uint32_t)g;
     auto issue = [&](int t) {
         const int rq = min(rr + t * nrr, nrq - 1);
-        const int64_t row = r0 + min(4 * rq + j, nrows - 1);
-        const int64_t co = row * rb + kNB * g - (int64_t)sh;
+        const uint32_t jj = (uint32_t)min(j, nrows - 1 - 4 * rq);
+        const int64_t row0 = r0 + 4 * rq;
+        const uint32_t co = jj * (uint32_t)rb + lane_co, so = jj * (uint32_t)(2 * p.ng) + lane_so;
 #pragma unroll
         for (int pl = 0; pl < PL; ++pl) {
-            C[t][pl] = __builtin_nontemporal_load((const u32x4a*)(p.codes[pl] + co));
-            S[t][pl] = p.scales[pl][row * p.ng + g];
+            const uint8_t* cb = p.codes[pl] + row0 * rb;
+            const uint8_t* sb = (const uint8_t*)p.scales[pl] + row0 * 2 * p.ng;
+            C[t][pl] = __builtin_nontemporal_load((const u32x4a*)(cb + co));
+            S[t][pl] = *(const uint16_t*)(sb + so);
         }
     };
     issue(0);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(3);
 
     // ---- stage x: token m's group q at m kXsTok + q kXsPitch
 #pragma unroll
@@ -288,7 +322,11 @@ __global__ void __launch_bounds__(kT, 1) tq_wave_dense_kernel(WaveParams p) {
         const int rq = rr + t * nrr;
         if (active && rq < nrq)
             decode_task<PL>(C[t], S[t], A, lut, cofs, sh, lane, red + (rq * nkq + kq) * kTaskStride);
+        // a wave that is ahead yields issue priority to those behind, so
+        // that the waves reach the barrier together
+        yield_after(t);
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     write_rows(red, nkq, nrows, p.M, r0, p.N, p.y, p.y_dtype, [](int m) { return (int64_t)m; });
 }
@@ -432,21 +470,27 @@ __device__ __forceinline__ void grouped_work(const WaveParams& p, unsigned char*
         }
     };
     // ---- task slot t: row quad tq of round r; lane (b, j) reads row j's
-    // group b of the round's expert and its scale.  Every slot is loaded, a
+    // group b of the round's expert and its scale (16 aligned bytes at
+    // 13 g - sh, as in the dense kernel).  Every slot is loaded, a
     // slot past the round's end with the round's last row quad (a cache
     // hit): a load under a branch would leave the wait counts unknown after
     // it, and the decode of a task would then wait for the next task's bytes.
+    // The row quad's first row is uniform (a scalar base address); a lane
+    // adds its own 32-bit offset.
     u32x4 C[4][PL];
     uint16_t S[4][PL];
+    const uint32_t lane_co = (uint32_t)(kNB * g) - sh, lane_so = 2u * (uint32_t)g;
     auto issue = [&](int t, const Round& r, int tq) {
-        const int64_t row = min((int64_t)4 * (r.rq + min(tq, r.len - 1)) + j, p.N - 1);
+        const int row0 = 4 * (r.rq + min(tq, r.len - 1));
+        const uint32_t jj = (uint32_t)min(j, (int)(p.N - 1 - row0));
         const int64_t e = p.e_begin + r.el;
-        const int64_t co = e * p.e_codes + row * rb + kNB * g - (int64_t)sh;
-        const int64_t so = e * p.e_scales + row * p.ng + g;
+        const uint32_t co = jj * (uint32_t)rb + lane_co, so = jj * (uint32_t)(2 * p.ng) + lane_so;
 #pragma unroll
         for (int pl = 0; pl < PL; ++pl) {
-            C[t][pl] = __builtin_nontemporal_load((const u32x4a*)(p.codes[pl] + co));
-            S[t][pl] = p.scales[pl][so];
+            const uint8_t* cb = p.codes[pl] + (e * p.e_codes + (int64_t)row0 * rb);
+            const uint8_t* sb = (const uint8_t*)p.scales[pl] + 2 * (e * p.e_scales + (int64_t)row0 * p.ng);
+            C[t][pl] = __builtin_nontemporal_load((const u32x4a*)(cb + co));
+            S[t][pl] = *(const uint16_t*)(sb + so);
         }
     };
 
@@ -458,6 +502,7 @@ __device__ __forceinline__ void grouped_work(const WaveParams& p, unsigned char*
         // counters retire in order, so waiting for x does not wait for it
         load_x(nt, pbase);
         issue(0, cur, rr);
+        issue(1, cur, rr + nrr);
         __builtin_amdgcn_sched_barrier(0);
         store_x(nt);
         __syncthreads();
@@ -470,29 +515,37 @@ __device__ __forceinline__ void grouped_work(const WaveParams& p, unsigned char*
                 a_seg = cur.seg;
                 build_a(xs, j, g, nt, A);
             }
-            // the next round; its activations go out now when its tokens differ
+            __builtin_amdgcn_s_setprio(3);
             const int qn = cur.q + cur.len;
             const bool more = qn < q1;
             Round nx = cur;
             int nnt = nt, npb = pbase;
             bool restage = false;
-            if (more) {
-                nx = locate(qn);
-                if (nx.seg != cur.seg) {
-                    restage = true;
-                    tokens(nx, nnt, npb);
-                    load_x(nnt, npb);
-                }
-            }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                // the next task's load goes out before this task is decoded
-                if (t < 3) issue(t + 1, cur, rr + (t + 1) * nrr);
-                else issue(0, nx, rr);                    // nx is cur after the last round
+                // the load two tasks ahead goes out before this task is
+                // decoded (the next round's first two from t = 2 on; nx is
+                // cur after the last round)
+                if (t < 2) issue(t + 2, cur, rr + (t + 2) * nrr);
+                else issue(t - 2, nx, rr + (t - 2) * nrr);
                 const int tq = rr + t * nrr;
                 if (active && tq < cur.len)
                     decode_task<PL>(C[t], S[t], A, lut, cofs, sh, lane, red + (tq * nkq + kq) * kTaskStride);
+                if (t == 0 && more) {
+                    // the next round; its activations go out now when its
+                    // tokens differ
+                    nx = locate(qn);
+                    if (nx.seg != cur.seg) {
+                        restage = true;
+                        tokens(nx, nnt, npb);
+                        load_x(nnt, npb);
+                    }
+                }
+                // a wave that is ahead yields issue priority to those behind,
+                // so that the waves reach the barrier together
+                yield_after(t);
             }
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             if (restage) store_x(nnt);
             const int nrows = (int)min((int64_t)4 * cur.len, p.N - 4 * (int64_t)cur.rq);
