@@ -18,7 +18,8 @@
 //    fp32 entry v is stored as two bf16 terms, hi = bf16(v) and
 //    lo = bf16(v - hi) (|v - hi - lo| <= 2^-17 |v|), packed as one dword.
 //    The table is replicated (64 copies in the general path, entry b of copy
-//    c at byte 256 b + 4 c; 16 in the tiled path) so that the lanes reading
+//    c at byte 256 b + 4 c; 32 in the tiled path, 16 when the activations
+//    are staged in LDS too) so that the lanes reading
 //    at once mostly hit distinct banks, and the address is a single v_perm
 //    of the code dword with the lane offset.
 //  * bf16 MFMA 16x16x32: B takes the looked-up (hi, lo) dword as two K-slots
@@ -45,7 +46,6 @@ constexpr int kTThreads = 64 * kTWaves;
 constexpr int kTileK = 64 * kTWaves;        // K bytes per tile
 constexpr int kTilePitch = kTileK + 16;     // padded LDS row pitch: column reads hit distinct banks
 constexpr int kTileBytes = 16 * kTilePitch;
-constexpr int kTCopies = 16;                // code-book copies in the tiled path
 static_assert(2 * kTileBytes >= kTWaves * 64 * 4 * 4, "reduction fits the tile buffers");
 constexpr int kLutBytes = 256 * 256;       // 256 entries x 64 copies x 4 B
 
@@ -326,17 +326,28 @@ rb_gemv_kernel(Params p) {
 // the direct loads are faster (M = 12: equal; M = 8: 19.4 against 22.0 us).
 constexpr int kXPitch = 2 * kTileK + 16;     // bytes per staged token row (8 lanes of a read phase hit distinct banks)
 constexpr int kXStageMinM = 13;
-template <bool XS>
-__global__ void __launch_bounds__(kTThreads, 2)
+// NB = 2: a workgroup of 16 waves owns two adjacent 16-row blocks (8 waves
+// each, one code book, one barrier per tile for all 16).  Two 8-wave
+// workgroups on one compute unit drift apart (the older one's waves win the
+// issue slots and it finishes about a fifth of the run earlier, leaving the
+// other alone on the compute unit); one workgroup keeps both blocks in step.
+template <bool XS, int NB>
+__global__ void __launch_bounds__(kTThreads * NB, 2 / NB)
 rb_gemv_tiled_kernel(Params p) {
+    // code-book copies: 64 for one workgroup a compute unit (NB = 2; the
+    // v_perm result is the address, every lane its own bank); for two, 32,
+    // or 16 when the staged activations share LDS
+    constexpr int kTCopies = NB == 2 ? 64 : (XS ? 16 : 32);
     __shared__ __attribute__((aligned(16))) unsigned char lut[256 * 4 * kTCopies];
-    __shared__ __attribute__((aligned(16))) unsigned char tiles[2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char tiles[2][NB][kTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char xtiles[XS ? 2 : 1][XS ? 16 * kXPitch : 16];
 
     const int tid = threadIdx.x;
-    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
+    const int wave_all = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
+    const int blk = wave_all / kTWaves;             // row block of this wave
+    const int wave = wave_all % kTWaves;            // its role in the block
     const int lane = tid & 63;
-    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * 16;
+    const int64_t row0 = (xcd_block(blockIdx.x, gridDim.x) * NB + blk) * 16;
     const int64_t ntiles = p.K / kTileK;          // >= 1: the launcher requires K >= kTileK
 
     // tile row this lane fetches (clamped into range), 16 bytes at 16 (lane & 31)
@@ -348,9 +359,10 @@ rb_gemv_tiled_kernel(Params p) {
     const int col = lane & 15;
     const int kb = lane >> 4;
     const uint16_t* xrow = p.x + (a_ok ? am : 0) * p.K + 64 * wave + 16 * kb;
-    // staged activations: thread tid loads token tid / 32 (clamped to M - 1),
-    // columns 16 (tid % 32) .. + 15 of the tile
-    const int xt = tid >> 5, xc = tid & 31;
+    // staged activations: thread tid (< 512) loads token tid / 32 (clamped
+    // to M - 1), columns 16 (tid % 32) .. + 15 of the tile; both blocks read
+    // the copy that block 0's threads store
+    const int xt = (tid >> 5) & 15, xc = tid & 31;
     const uint16_t* xsrc = p.x + min((int64_t)xt, p.M - 1) * p.K + 16 * xc;
 
     struct Stage {
@@ -368,37 +380,41 @@ rb_gemv_tiled_kernel(Params p) {
 
     // the code-book read goes first so that waiting for it leaves the tile
     // loads in flight (memory counters complete in order)
-    const int lb = tid >> 1;
+    const int lb = tid / (2 * NB);
     const float tv = rb_table_of(p.table, p.table_rows, row0)[lb < 243 ? lb : 0];
     Stage s0, s1;
     fetch(0, s0);
     fetch(1, s1);
 
-    {   // entry b, copies 8 (tid & 1) .. + 7; entries 243..255 read zero
+    {   // entry b, copies kTCopies / (2 NB) (tid % 2 NB) .. ; entries 243..255 read zero
         const uint32_t e = split_bf16_pair(lb < 243 ? tv : 0.f);
         const u32x4 q = {e, e, e, e};
-        unsigned char* base = lut + lb * 4 * kTCopies + (tid & 1) * 2 * kTCopies;
-        *(u32x4*)base = q;
-        *(u32x4*)(base + 16) = q;
+        unsigned char* base = lut + lb * 4 * kTCopies + (tid % (2 * NB)) * 2 * kTCopies / NB;
+#pragma unroll
+        for (int i = 0; i < kTCopies / (8 * NB); ++i) *(u32x4*)(base + 16 * i) = q;
     }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // entry b, copy c at byte 64 b + 4 c; lane l reads copy l % 16: the
-    // v_perm below forms 256 b + 16 (l % 16), shifted right by two
-    const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
+    // entry b, copy c at byte 4 kTCopies b + 4 c; lane l reads copy
+    // l % kTCopies: the v_perm below forms 256 b + (256 / kTCopies) (l % kTCopies),
+    // shifted right by 6 - log2(kTCopies)
+    constexpr uint32_t kCopyShift = kTCopies == 64 ? 0u : (kTCopies == 32 ? 1u : 2u);  // 6 - log2(kTCopies)
+    const uint32_t lane_off = (uint32_t)(lane & (kTCopies - 1)) << (2 + kCopyShift);
 
     // tile t goes to LDS buffer t & 1: the barrier after writing tile t also
     // orders every read of tile t - 2 (same buffer) before its overwrite
     auto step = [&](const Stage& S, int buf) {
         // keep the next stage's work (it waits on younger loads) out of this step
         __builtin_amdgcn_sched_barrier(0);
-        unsigned char* tile = tiles[buf];
+        unsigned char* tile = tiles[buf][blk];
         *(u32x4*)(tile + lrow * kTilePitch + 16 * (lane & 31)) = u32x4{S.c.x, S.c.y, S.c.z, S.c.w};
         uint32_t XV[8];
         if constexpr (XS) {
-            unsigned char* xb = xtiles[buf] + xt * kXPitch + 32 * xc;
-            *(u32x4*)xb = u32x4{S.X[0], S.X[1], S.X[2], S.X[3]};
-            *(u32x4*)(xb + 16) = u32x4{S.X[4], S.X[5], S.X[6], S.X[7]};
+            if (blk == 0) {
+                unsigned char* xb = xtiles[buf] + xt * kXPitch + 32 * xc;
+                *(u32x4*)xb = u32x4{S.X[0], S.X[1], S.X[2], S.X[3]};
+                *(u32x4*)(xb + 16) = u32x4{S.X[4], S.X[5], S.X[6], S.X[7]};
+            }
         }
         __syncthreads();
         const u32x4 v = *(const u32x4*)(tile + col * kTilePitch + 64 * wave + 16 * kb);
@@ -425,7 +441,7 @@ rb_gemv_tiled_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t addr =
-                    perm_b32(D[j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8)) >> 2;
+                    perm_b32(D[j], lane_off, 0x0c0c0400u + ((uint32_t)i << 8)) >> kCopyShift;
                 bq[i] = *(const uint32_t*)(lut + addr);
             }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aq),
@@ -443,9 +459,9 @@ rb_gemv_tiled_kernel(Params p) {
     }
     if (t < ntiles) step(s0, 0);
 
-    // partials of the 8 waves meet in the (now idle) tile buffers
+    // partials of a block's 8 waves meet in its (now idle) tile buffer
     __syncthreads();
-    float* red = (float*)tiles[0];                                // [kTWaves][64][4]
+    float* red = (float*)tiles[0][blk];                           // [kTWaves][64][4]
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
     __syncthreads();
@@ -469,6 +485,19 @@ rb_gemv_tiled_kernel(Params p) {
             }
         }
     }
+}
+
+int rb_compute_units() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
 }
 
 }  // namespace
@@ -501,12 +530,19 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
     const bool tiled = a.K >= kTileK && (a.K % kTileK == 0) &&
                        (((uintptr_t)a.codes & 15) == 0) && (((uintptr_t)a.x & 3) == 0);
     if (tiled) {
-        if (a.M >= kXStageMinM)
-            hipLaunchKernelGGL(rb_gemv_tiled_kernel<true>, dim3((unsigned)((a.N + 15) / 16)),
-                               dim3(kTThreads), 0, s, p);
-        else
-            hipLaunchKernelGGL(rb_gemv_tiled_kernel<false>, dim3((unsigned)((a.N + 15) / 16)),
-                               dim3(kTThreads), 0, s, p);
+        // two row blocks a workgroup when that still gives every compute unit
+        // one, and both blocks use one code book
+        const int64_t nblk = (a.N + 15) / 16;
+        const bool pair = nblk >= 2 * (int64_t)rb_compute_units() &&
+                          (a.table_rows == 0 || a.table_rows % 32 == 0);
+        const dim3 g1((unsigned)nblk), g2((unsigned)((nblk + 1) / 2));
+        if (a.M >= kXStageMinM) {
+            if (pair) hipLaunchKernelGGL((rb_gemv_tiled_kernel<true, 2>), g2, dim3(2 * kTThreads), 0, s, p);
+            else hipLaunchKernelGGL((rb_gemv_tiled_kernel<true, 1>), g1, dim3(kTThreads), 0, s, p);
+        } else {
+            if (pair) hipLaunchKernelGGL((rb_gemv_tiled_kernel<false, 2>), g2, dim3(2 * kTThreads), 0, s, p);
+            else hipLaunchKernelGGL((rb_gemv_tiled_kernel<false, 1>), g1, dim3(kTThreads), 0, s, p);
+        }
         return hipGetLastError();
     }
     const bool aligned4 = (((uintptr_t)a.codes & 3) == 0) && (a.K % 4 == 0);
