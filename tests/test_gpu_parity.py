@@ -623,6 +623,42 @@ def test_rb_matmul_tiled_shapes(dmm, M, N, K):
     rb_case(dmm, M, N, K, seed=M + 5 * N + K, ydt=torch.bfloat16, rho=True, bias=True)
 
 
+# Shapes of the wave-local GEMV form (1 to 4 tokens, K % 256 == 0, aligned
+# operands): one row quad split over 16 waves (N = 4), 1000 rows (one row
+# quad a workgroup), 5000 rows (5 row quads, K split 3 ways unevenly), a
+# ragged last workgroup (8190), several row quads a wave (70000 rows), a
+# partial last row quad (257) and a single K step (K = 256).
+RB_WAVE_CASES = [
+    (1, 4, 4096), (2, 1000, 256), (3, 5000, 1792), (4, 8190, 2048), (1, 70000, 256),
+    (4, 257, 768), (2, 3, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", RB_WAVE_CASES)
+def test_rb_matmul_wave_shapes(dmm, M, N, K):
+    rb_case(dmm, M, N, K, seed=M * 13 + N + K, bad_codes=True)
+    rb_case(dmm, M, N, K, seed=M + 3 * N + K, ydt=torch.bfloat16, rho=True, bias=True)
+
+
+def test_rb_matmul_wave_per_block_books(dmm):
+    """One code book per 32 rows on the wave-local form (a workgroup's rows
+    lie in one book): N = 8192 (32 rows a workgroup) and N = 1000 (4)."""
+    rng = np.random.default_rng(77)
+    for N, K, M in ((8192, 512, 2), (1000, 1024, 4)):
+        codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
+        nb = -(-N // 32)
+        tables = np.stack([oracle.rb_table((S_LADDER * rng.uniform(0.5, 2.0)).astype(np.float32))
+                           for _ in range(nb)])
+        xb = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        say(f"rb_matmul_blocks wave N={N} K={K} M={M}")
+        dmm.rb_matmul_blocks(dev(bits16(xb)), dev(codes), dev(tables.reshape(-1)), 32, 0.02, y)
+        w = np.concatenate([oracle.rb_weights(codes[h * 32:(h + 1) * 32], tables[h], np.float32(0.02))
+                            for h in range(nb)])
+        y_ref, B = oracle.matmul_ref(xb, w)
+        assert_bound(y_host(y), y_ref, B, f"blocks wave N={N}")
+
+
 @pytest.mark.parametrize("code_off,x_off", [(1, 1), (2, 0), (3, 3)])
 def test_rb_matmul_offsets_and_bad_codes(dmm, code_off, x_off):
     rb_case(dmm, 4, 50, 256, 31, code_off=code_off, x_off=x_off, bad_codes=True)
