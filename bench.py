@@ -40,10 +40,10 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 # HBM bytes of one headline launch (M = 1) from the hardware byte counters
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the factors that make a 512 MiB device
-# copy read and write 512 MiB), in profiles/hbm_traffic_rb_gemv_tq_rows.md.
+# copy read and write 512 MiB), in profiles/hbm_traffic_rb_gemv_tq_wave.md.
 # The figure belongs to the kernel source it was measured on: any other
 # source of rb_gemv.hip reports null.
-MEASURED_TRAFFIC = {"rb_gemv.hip": ("7c9c632fe5bc66fb", 67367029)}
+MEASURED_TRAFFIC = {"rb_gemv.hip": ("6edb423a5a96f60d", 67360886)}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "packed matmul: weight GB/s vs HBM peak at M=1–16; TFLOP/s at M=2048"
 
