@@ -3,8 +3,8 @@
 // Semantics: "A Discrete Weight Language for Large Language Models" (Route
 // B), section 3.2 (codes index a 243-entry code book), section 3.3 (per-row
 // scale rho_n) and section 4.2 (the code book sits in on-chip memory, every
-// code byte is dereferenced through it inside a K-sliced GEMM, rho_n is
-// applied to the accumulator before the bias).  With per-block code books
+// code byte is dereferenced through it inside a K-sliced GEMM; rho_n
+// multiplies the finished sum and the bias comes after it).  With per-block code books
 // (section 8.3: one ladder per block of 32 rows) T is the book of the row's
 // block; a workgroup's rows lie in one block, so it stages that one.
 //

@@ -3,8 +3,8 @@
 //
 // Semantics: "A Discrete Weight Language for Large Language Models" (Route
 // B), section 4.2: the code book is loaded on chip once per block and a
-// K-sliced GEMM dereferences every code byte through it; rho_n is applied to
-// the output accumulator before the bias add (section 3.3).
+// K-sliced GEMM dereferences every code byte through it; y = alpha rho_n acc
+// + bias_n, so rho multiplies the finished sum (sections 3.3 and 4.2).
 //
 // Numerics.  The products run on fp16 MFMAs with fp32 accumulation:
 //  * The code book is scaled by sigma = 2^j so that max |sigma T| lies in

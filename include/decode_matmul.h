@@ -265,9 +265,9 @@ int rb_encode(const float* W, int64_t N, int64_t K, const float* ladder, float z
               int32_t* d_status, void* stream);
 
 /*
- * rb_matmul -- Route B matmul (Route B paper, section 4.2: code bytes are
- * dereferenced through the code book inside the GEMM; the per-row scale is
- * applied to the output accumulator before the bias add):
+ * rb_matmul -- Route B matmul (Route B paper, sections 3.3 and 4.2: each code
+ * byte is looked up in the code book inside the GEMM, and the row's scale
+ * multiplies the finished sum, with the bias added last):
  *
  *     y[m, n] = alpha * rho_n * sum_k x[m, k] * table[codes[n, k]]  (+ bias[n])
  *
