@@ -180,6 +180,10 @@ bool launch_tq_rows(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
 // most 256 (token, slot) pairs (G = 64, K = 1024..4096 in steps of 1024);
 // false when the call is outside its domain.
 bool launch_tq_wave(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
+// Dense calls of 5..16 tokens on full-width MFMAs (one plane, G = 64,
+// K = 256, 512, 1024, 2048 or 4096; x, codes and scales 4-byte aligned);
+// false when the call is outside its domain.
+bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err);
 // A hot-prefix call (two-plane hot launch, one-plane cold launch that writes
 // the invalid-id rows) as one wave-local launch; false outside its domain.
 bool launch_tq_wave_hot(const TqMatmulArgs& hot, const TqMatmulArgs& cold, hipStream_t s,

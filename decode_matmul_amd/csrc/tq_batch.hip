@@ -1,0 +1,342 @@
+// Ternary GEMV for 5 to 16 dense tokens: y = x (s T)^T with G = 64 and one
+// plane, decoded inside the kernel.
+//
+// Format: pack-unpack-run, "Five trits in a byte" (five base-3 digits per
+// byte, least significant first) and "Three values and a shared scale"
+// (W_hat = s t per group of 64).
+//
+// A wave owns a slice of four groups of K and walks the 16-row blocks of its
+// workgroup's rows; its activations for the slice stay in registers.  The
+// multiply is the 16x16x32 bf16 MFMA at full width (16 tokens x 16 rows),
+// with one accumulator per group so that the group's fp16 scale is applied
+// in fp32:
+//  * lane (c, r) = (lane / 16, lane % 16) supplies row r (B) or token r (A)
+//    and K-chunk c of each MFMA.  Within a group it owns trits 16c .. 16c+15,
+//    which all lie in the four bytes 3c .. 3c+3: one unaligned dword.
+//  * its B operands hold every digit of those four bytes in a fixed order:
+//    digits 0..3 of bytes 0, 1 (first 16x16x32 MFMA) and of bytes 2, 3
+//    (second) from an LDS code book of ready bf16 pairs, then digit 4 of
+//    bytes 0, 2, 1, 3 (a 16x16x16 MFMA) from packed 16-bit arithmetic;
+//  * its A operands hold the activations of the same K positions, and zero
+//    where a digit belongs to the neighbouring lane (bytes 3c and 3c+3 are
+//    shared) or to the padding, so every trit is counted once;
+//  * the group's sum is scaled by its fp16 scale in fp32 and added to the
+//    lane's 4 tokens of row r.
+// The partial sums of the K slices meet in LDS and are added in a fixed
+// order, so results are bit-reproducible.
+#include "common.h"
+#include "tq_book.h"
+
+namespace dmm {
+
+namespace {
+
+constexpr int kW = 16;
+constexpr int kT = 64 * kW;
+constexpr int kNB = 13;                  // code bytes per group of 64 trits
+constexpr int kPart = 64 * 4;            // floats of one wave's partial sums
+constexpr int kTileBytes = 17920;        // code + scale tile of a super-block, largest K
+constexpr int kBookBytes = 256 * 256;    // code book: 256 entries x 32 copies x 8 bytes
+constexpr int kRedBytes = kW * kPart * 4;  // partial sums of a super-block
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+
+struct BatchParams {
+    const uint16_t* x;
+    int64_t K, N;
+    int ng, M;
+    const uint8_t* codes;
+    const uint16_t* scales;
+    uint32_t code_bytes;         // N * ng * 13
+    uint32_t scale_bytes;        // N * ng * 2
+    int pitch, spitch;           // LDS bytes of a code / scale row of a tile
+    int lnks;                    // log2 of the 4-group slices of K
+    int lT;                      // log2 of the lanes that add up one output
+    int rows_per_wg;
+    void* y;
+    int y_dtype;
+};
+
+// Operands of one group on one lane: A0, A1 (16x16x32) and A2 (16x16x16).
+struct GroupA {
+    u32x4 a0, a1;
+    u32x2 a2;
+};
+
+// Activations of lane (c, t) for group g: elements 64 g + 15 c .. + 18 of
+// token t's row, as the ten dwords from the even element at or below the
+// first (all inside the group).
+__device__ __forceinline__ void load_group_x(const uint16_t* xrow, int g, int c, uint32_t (&X)[10]) {
+    const uint16_t* p = xrow + ((64 * g + 15 * c) & ~1);
+    const u32x4 v0 = *(const u32x4a*)(p), v1 = *(const u32x4a*)(p + 8);
+    const u32x2 v2 = *(const u32x2a*)(p + 16);
+    X[0] = v0.x; X[1] = v0.y; X[2] = v0.z; X[3] = v0.w;
+    X[4] = v1.x; X[5] = v1.y; X[6] = v1.z; X[7] = v1.w;
+    X[8] = v2.x; X[9] = v2.y;
+}
+
+// Masks of the lane's A operands: digits of the first byte below c and of
+// the last byte above c are the neighbours'.  (Rows of A past M need no
+// mask: they only reach rows of the product that are never written.)
+struct AMask {
+    uint32_t m0, m1, m6, m7;
+};
+
+__device__ __forceinline__ AMask a_masks(int c) {
+    AMask k;
+    k.m0 = (c <= 0 ? 0x0000FFFFu : 0u) | (c <= 1 ? 0xFFFF0000u : 0u);
+    k.m1 = (c <= 2 ? 0x0000FFFFu : 0u) | 0xFFFF0000u;
+    k.m6 = 0x0000FFFFu | (c >= 1 ? 0xFFFF0000u : 0u);
+    k.m7 = (c >= 2 ? 0x0000FFFFu : 0u) | (c >= 3 ? 0xFFFF0000u : 0u);
+    return k;
+}
+
+// The lane's A operands for one group, in the K order of its B operands:
+// element 15 c + 5 j + d of the group for digit d of byte j, zero where the
+// trit is not the lane's (the first byte's digits below c, the last byte's
+// digits above c, the last byte's digit 4).
+__device__ __forceinline__ GroupA build_group_a(const uint32_t (&X)[10], uint32_t sh, const AMask& k) {
+    uint32_t Y[10];                                    // Y[q]: elements 2q, 2q + 1 of the lane's run
+#pragma unroll
+    for (int q = 0; q < 10; ++q) Y[q] = align_bytes(q + 1 < 10 ? X[q + 1] : 0u, X[q], sh);
+    GroupA A;
+    // digits 0..3 of bytes 0, 1: elements 0..3, 5..8
+    A.a0 = u32x4{Y[0] & k.m0, Y[1] & k.m1, align_bytes(Y[3], Y[2], 2), align_bytes(Y[4], Y[3], 2)};
+    // digits 0..3 of bytes 2, 3: elements 10..13, 15..18
+    A.a1 = u32x4{Y[5], Y[6], align_bytes(Y[8], Y[7], 2) & k.m6, align_bytes(Y[9], Y[8], 2) & k.m7};
+    // digit 4 of bytes 0, 2 | 1, 3: elements 4, 14 | 9 (byte 3's is not the lane's)
+    A.a2 = u32x2{perm_b32(Y[7], Y[2], 0x05040100u), Y[4] >> 16};
+    return A;
+}
+
+// Workgroup w owns rows [w rows_per_wg, ...), taken in super-blocks of
+// 16 nrs rows (13 KB of codes and 2 KB of scales at every K).  A super-block
+// is loaded with coalesced 16-byte pieces, two super-blocks ahead, and stored
+// to an LDS tile; after one barrier wave (ks, rs) multiplies 16-row block rs
+// of it by the 4-group slice ks of K.  The slices' partial sums of a
+// super-block are added up after the next barrier, by all waves.
+__global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
+    // code book at LDS address 0 (a lookup address is one v_perm), then two
+    // tiles and two sets of partial sums
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kBookBytes + 2 * kTileBytes + 2 * kRedBytes];
+    unsigned char* const lut = smem;
+    unsigned char* const tiles = smem + kBookBytes;
+    float* const red = (float*)(smem + kBookBytes + 2 * kTileBytes);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = readfirstlane(tid >> 6);
+    const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_wg;
+    const int nrows = (int)(min(r0 + (int64_t)p.rows_per_wg, p.N) - r0);
+    const int lnks = p.lnks;                          // log2 of the 4-group slices of K (2, 3, 4)
+    const int nks = 1 << lnks;
+    const int ks = wave & (nks - 1), rs = wave >> lnks;
+    const int lsbr = 8 - lnks;                        // super-block rows 16 nrs = 256 / nks
+    const int sbr = 1 << lsbr;
+    const int nsb = (nrows + sbr - 1) >> lsbr;
+    const int c = lane >> 4, r = lane & 15;
+    const uint32_t rb = (uint32_t)p.ng * kNB;         // code bytes of a row
+    const uint32_t sbb = rb << lsbr;                  // code bytes of a super-block (13312)
+    const uint32_t sbs = (uint32_t)p.ng << (lsbr + 1);   // scale bytes (2048)
+
+    // ---- thread tid moves piece tid of a super-block: code pieces first
+    // (sbb / 16 of them), then scale pieces; the address is clamped into the
+    // arrays (rows past N are loaded from the end and never written out)
+    const int ncp = (int)(sbb >> 4);
+    const bool is_code = tid < ncp;
+    const int sp = tid - ncp;                         // scale piece when >= 0
+    const bool stores = is_code || sp < (int)(sbs >> 4);
+    const uint8_t* src = is_code ? p.codes : (const uint8_t*)p.scales;
+    const uint32_t src_end = is_code ? p.code_bytes : p.scale_bytes;
+    const uint32_t src_sb = is_code ? sbb : sbs;
+    const uint32_t piece = (uint32_t)(is_code ? tid : (stores ? sp : 0));
+    const uint32_t src_wg = (uint32_t)r0 * (src_sb >> lsbr);   // first byte of the workgroup
+    auto load_sb = [&](int k) {
+        const uint32_t o = min(src_wg + (uint32_t)k * src_sb + 16u * piece, src_end - 16u);
+        return __builtin_nontemporal_load((const u32x4a*)(src + o));
+    };
+    u32x4 R0 = load_sb(0), R1 = load_sb(1);
+
+    // ---- activations of the slice (memory counters retire in order: the
+    // first super-blocks go out ahead of them)
+    uint32_t XR[4][10];
+    {
+        // token r; rows of A past M read token 0 and feed unwritten outputs
+        const uint16_t* xrow = p.x + (int64_t)(r < p.M ? r : 0) * p.K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_group_x(xrow, 4 * ks + i, c, XR[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fill_book(lut, tid);
+
+    // LDS destination of the piece in a tile: row-padded code rows, then
+    // row-padded scale rows (conflict-free reads)
+    uint32_t dst;
+    {
+        const int cpr = (int)(rb >> 4), spr = p.ng >> 3;   // 16-byte pieces of a row
+        if (is_code) {
+            const int row = tid / cpr;
+            dst = (uint32_t)(row * p.pitch + 16 * (tid - row * cpr));
+        } else {
+            const int row = (int)piece / spr;
+            dst = (uint32_t)((sbr * p.pitch) + row * p.spitch + 16 * ((int)piece - row * spr));
+        }
+    }
+    GroupA A[4];
+    {
+        const AMask mk = a_masks(c);
+        const uint32_t sh = 2u * (uint32_t)(c & 1);    // the lane's first element is odd when c is
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[i] = build_group_a(XR[i], sh, mk);
+    }
+    const uint32_t cofs = (uint32_t)(lane & 31) << 3;    // code-book copy lane % 32
+
+    // ---- reduction of super-block k by every thread: output (m, n) takes
+    // lanes q = tid & (T - 1) of a group of T, which add slices q, q + T, ...
+    // and then sum across the group in a fixed order
+    const int lT = p.lT, T = 1 << lT;
+    auto reduce = [&](int k) {
+        const float* rk = red + (k & 1) * kW * kPart;
+        const int rows = min(sbr, nrows - (k << lsbr));
+        const int q = tid & (T - 1);
+        for (int o0 = 0; o0 < (p.M << lsbr); o0 += kT >> lT) {
+            const int o = o0 + (tid >> lT);
+            const int n = o & (sbr - 1), m = o >> lsbr;
+            float sum = 0.f;
+            if (m < p.M) {
+                const float* src_p = rk + ((n >> 4) << lnks) * kPart + 4 * (16 * (m >> 2) + (n & 15)) + (m & 3);
+                for (int w = q; w < nks; w += T) sum += src_p[w * kPart];
+            }
+            // groups of T consecutive lanes: pairwise in a fixed order
+            if (T >= 2) sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, true));
+            if (T >= 4) sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, true));
+            if (q == 0 && m < p.M && n < rows) {
+                const float v = 0.5f * sum;           // the code book holds 2t
+                const int64_t yi = (int64_t)m * p.N + r0 + ((int64_t)k << lsbr) + n;
+                if (p.y_dtype == TQ_F32) ((float*)p.y)[yi] = v;
+                else ((uint16_t*)p.y)[yi] = f32_to_bf16_rne(v);
+            }
+        }
+    };
+
+    // super-block k: store the pieces loaded two steps ago, load k + 2 into
+    // the same registers, one barrier, then the previous super-block's sums
+    // and this one's products
+    auto step = [&](int k, u32x4& R) {
+        unsigned char* tile = tiles + (k & 1) * kTileBytes;
+        const bool live = k < nsb;                    // uniform
+        if (live && stores) {
+            *(u32x2*)(tile + dst) = u32x2{R.x, R.y};
+            *(u32x2*)(tile + dst + 8) = u32x2{R.z, R.w};
+        }
+        R = load_sb(k + 2);
+        if (!live) return;
+        __syncthreads();
+        if (k > 0) reduce(k - 1);
+        if ((rs << 4) < nrows - (k << lsbr)) {
+            const unsigned char* trow = tile + ((rs << 4) + r) * p.pitch;
+            const unsigned char* srow = tile + (sbr * p.pitch) + ((rs << 4) + r) * p.spitch;
+            const u32x2 S = *(const u32x2*)(srow + 8 * ks);
+            f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t byte = (uint32_t)(kNB * (4 * ks + i) + 3 * c);
+                const u32x2 d = *(const u32x2a*)(trow + (byte & ~3u));
+                const uint32_t W = align_bytes(d.y, d.x, byte & 3u);
+                const uint2 e0 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0400u));
+                const uint2 e1 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0500u));
+                const uint2 e2 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0600u));
+                const uint2 e3 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0700u));
+                f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, A[i].a0), __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y}),
+                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, A[i].a1), __builtin_bit_cast(bf16x8, u32x4{e2.x, e2.y, e3.x, e3.y}),
+                    acc, 0, 0, 0);
+                // digit 4 of bytes (0, 2) and (1, 3)
+                const u32x2 q = {t4pair(W & 0x00FF00FFu), t4pair(perm_b32(W, W, 0x0c030c01u))};
+                acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, A[i].a2),
+                                                                __builtin_bit_cast(bf16x4, q), acc, 0, 0, 0);
+                const uint32_t sw = (i < 2 ? S.x : S.y) >> (16 * (i & 1));
+                const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sw);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) tot[v] = __builtin_fmaf(sc, acc[v], tot[v]);
+            }
+            // D[4 c + v][r]: tokens 4c .. 4c+3 of row r of the block
+            *(f32x4*)(red + ((k & 1) * kW + wave) * kPart + 4 * lane) = tot;
+        }
+    };
+    // two steps a trip, so that super-blocks k and k + 1 stay in their own
+    // registers; every load is issued (past the end they are not used), so
+    // that each wait is for the older super-block only
+    for (int k = 0; k < nsb; k += 2) {
+        step(k, R0);
+        step(k + 1, R1);
+    }
+    __syncthreads();
+    reduce(nsb - 1);
+}
+
+int batch_compute_units() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+}  // namespace
+
+bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
+    if (a.G != 64 || a.n_experts != 0 || a.planes != 1 || a.M < 5 || a.M > 16 || a.N < 1) return false;
+    const int64_t ng = a.K / 64;
+    // 4-group slices of K: 4, 8 or 16 (code rows of a multiple of 16 bytes)
+    if (a.K != 1024 && a.K != 2048 && a.K != 4096) return false;
+    if (((uintptr_t)a.x & 3) != 0 || ((uintptr_t)a.codes[0] & 3) != 0 ||
+        ((uintptr_t)a.scales[0] & 3) != 0)
+        return false;
+    if (a.N * ng * kNB >= (1ll << 31)) return false;   // 32-bit byte offsets
+    BatchParams p;
+    p.x = a.x;
+    p.K = a.K;
+    p.N = a.N;
+    p.ng = (int)ng;
+    p.M = (int)a.M;
+    p.codes = a.codes[0];
+    p.scales = a.scales[0];
+    p.code_bytes = (uint32_t)(a.N * ng * kNB);
+    p.scale_bytes = (uint32_t)(a.N * ng * 2);
+    // code rows: a multiple of 16 bytes, at least 4 past the row, and
+    // pitch / 4 == 4 (mod 8) so that 16 rows start in distinct bank quads;
+    // scale rows: pitch / 4 == 2 (mod 4) for 8-byte reads of 16 rows
+    const int rb = (int)ng * kNB;
+    int pd = (rb + 4 + 3) / 4;
+    while (pd % 8 != 4) ++pd;
+    p.pitch = 4 * pd;
+    p.spitch = 4 * ((int)ng / 2 + 2);
+    p.lnks = ng == 16 ? 2 : ng == 32 ? 3 : 4;
+    const int nrs = kW >> p.lnks;
+    if (16 * nrs * (p.pitch + p.spitch) > kTileBytes) return false;
+    // lanes per output: the outputs of a super-block (M x 16 nrs) times the
+    // lanes fit the workgroup, at most 4 and at most the slices
+    const int outs = (int)a.M * 16 * nrs;
+    p.lT = outs * 4 <= kT ? 2 : outs * 2 <= kT ? 1 : 0;
+    const int cus = batch_compute_units();
+    const int64_t rpw = (a.N + cus - 1) / cus;
+    p.rows_per_wg = (int)rpw;
+    p.y = a.y;
+    p.y_dtype = a.y_dtype;
+    const int64_t wgs = (a.N + rpw - 1) / rpw;
+    hipLaunchKernelGGL(tq_batch_kernel, dim3((unsigned)wgs), dim3(kT), 0, s, p);
+    *err = hipGetLastError();
+    return true;
+}
+
+}  // namespace dmm

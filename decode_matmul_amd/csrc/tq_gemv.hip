@@ -396,6 +396,7 @@ hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s) {
         // the streaming form writes the rows of out-of-range expert ids itself
         hipError_t e;
         if (launch_tq_wave(a, s, &e)) return e;
+        if (launch_tq_batch(a, s, &e)) return e;
         if (launch_tq_rows(a, s, &e)) return e;
         if (launch_tq_prefill(a, s, &e)) return e;
     }

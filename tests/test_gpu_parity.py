@@ -300,6 +300,32 @@ def test_tq_matmul_streaming_shapes(dmm, M, N, K, planes):
         tq_case(dmm, M, N, K, 64, planes, ydt, seed=7 * M + N + K)
 
 
+# Shapes of the full-width form (dense, one plane, 5 to 16 tokens, K = 1024,
+# 2048 or 4096, super-blocks of 64, 32 or 16 rows): one row, rows that end
+# inside a 16-row block and inside a super-block, workgroups of one to many
+# super-blocks, and the last row's last group (the last code piece of the
+# array is read clamped).
+TQ_BATCH_CASES = [
+    (5, 1, 1024), (16, 17, 2048), (6, 1000, 1024), (9, 777, 2048), (12, 4100, 4096),
+    (16, 70000, 1024), (16, 40000, 4096), (5, 3, 4096), (13, 300, 1024), (7, 16, 2048),
+    (16, 14336, 4096), (11, 257, 4096), (16, 65, 1024), (8, 33000, 2048),
+]
+
+
+@pytest.mark.parametrize("M,N,K", TQ_BATCH_CASES)
+def test_tq_matmul_batch_shapes(dmm, M, N, K):
+    for ydt in (torch.float32, torch.bfloat16):
+        tq_case(dmm, M, N, K, 64, 1, ydt, seed=3 * M + N + K)
+
+
+def test_tq_matmul_batch_extreme_activations(dmm):
+    """Activations far outside fp16's range (tiny and huge) and zeros: the
+    full-width form multiplies in bf16 against exact 2t, so every value is
+    used as it is."""
+    for M, N, K in ((16, 300, 1024), (5, 64, 4096)):
+        tq_case(dmm, M, N, K, 64, 1, torch.float32, seed=M + K, x_special=True)
+
+
 @pytest.mark.parametrize("code_off,x_off", [(1, 0), (2, 2), (3, 4), (5, 6), (0, 1), (7, 3)])
 def test_tq_matmul_offset_views(dmm, code_off, x_off):
     """Non-zero view offsets of codes (any byte) and x (any element, odd ones
@@ -793,7 +819,8 @@ def test_zero_sizes_and_empty_k(dmm):
 def test_bit_determinism(dmm):
     """Two runs of every kernel family give identical bits (fixed-order
     reductions, no atomics on the accumulation path): dense ternary GEMV
-    (streaming and general forms), grouped two-plane experts, the hot
+    (wave-local form at 4 tokens, full-width form at 9), grouped two-plane
+    experts, the hot
     prefix, the ternary prefill (with and without a workspace), the Route B
     GEMV and prefill, per-block code books, 7-bit indices, the packer and
     the encoder."""
