@@ -34,10 +34,12 @@ namespace {
 constexpr int kW = 16;
 constexpr int kT = 64 * kW;
 constexpr int kNB = 13;                  // code bytes per group of 64 trits
-constexpr int kPart = 64 * 4;            // floats of one wave's partial sums
+constexpr int kPart = 64 * 4 + 4;        // floats of one wave's partial sums (+4: the slices
+                                         // a lane group adds sit in distinct banks)
 constexpr int kTileBytes = 17920;        // code + scale tile of a super-block, largest K
 constexpr int kBookBytes = 256 * 256;    // code book: 256 entries x 32 copies x 8 bytes
 constexpr int kRedBytes = kW * kPart * 4;  // partial sums of a super-block
+constexpr int kXPieces = 8;              // 16-byte pieces of x per thread: 16 tokens x 4096
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -54,6 +56,8 @@ struct BatchParams {
     int pitch, spitch;           // LDS bytes of a code / scale row of a tile
     int lnks;                    // log2 of the 4-group slices of K
     int lT;                      // log2 of the lanes that add up one output
+    int lxpr;                    // log2 of the 16-byte pieces of a row of x
+    int xpitch;                  // LDS bytes of a staged row of x
     int rows_per_wg;
     void* y;
     int y_dtype;
@@ -67,14 +71,15 @@ struct GroupA {
 
 // Activations of lane (c, t) for group g: elements 64 g + 15 c .. + 18 of
 // token t's row, as the ten dwords from the even element at or below the
-// first (all inside the group).
-__device__ __forceinline__ void load_group_x(const uint16_t* xrow, int g, int c, uint32_t (&X)[10]) {
-    const uint16_t* p = xrow + ((64 * g + 15 * c) & ~1);
-    const u32x4 v0 = *(const u32x4a*)(p), v1 = *(const u32x4a*)(p + 8);
-    const u32x2 v2 = *(const u32x2a*)(p + 16);
-    X[0] = v0.x; X[1] = v0.y; X[2] = v0.z; X[3] = v0.w;
-    X[4] = v1.x; X[5] = v1.y; X[6] = v1.z; X[7] = v1.w;
-    X[8] = v2.x; X[9] = v2.y;
+// first (all inside the group), read from the row staged in LDS at xs.
+__device__ __forceinline__ void load_group_x(const unsigned char* xs, int g, int c, uint32_t (&X)[10]) {
+    const unsigned char* p = xs + 2 * ((64 * g + 15 * c) & ~1);
+#pragma unroll
+    for (int q = 0; q < 10; q += 2) {
+        const u32x2 v = *(const u32x2a*)(p + 4 * q);
+        X[q] = v.x;
+        X[q + 1] = v.y;
+    }
 }
 
 // Masks of the lane's A operands: digits of the first byte below c and of
@@ -158,16 +163,44 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     };
     u32x4 R0 = load_sb(0), R1 = load_sb(1);
 
-    // ---- activations of the slice (memory counters retire in order: the
-    // first super-blocks go out ahead of them)
-    uint32_t XR[4][10];
+    // ---- activations: x goes through LDS (the whole shared space, before
+    // the code book is filled), loaded as coalesced 16-byte pieces; token
+    // rows are padded by 16 bytes so that the 16 tokens fall in distinct
+    // banks.  Memory counters retire in order: the first super-blocks went
+    // out ahead of the pieces.
+    {
+        const int lpr = p.lxpr;                       // log2 of the 16-byte pieces of a row
+        const int xp = p.M << lpr;
+        u32x4 XP[kXPieces];
+#pragma unroll
+        for (int j = 0; j < kXPieces; ++j) {
+            const int q = min(tid + kT * j, xp - 1);
+            XP[j] = *(const u32x4a*)(p.x + 8 * (int64_t)q);
+        }
+#pragma unroll
+        for (int j = 0; j < kXPieces; ++j) {
+            const int q = tid + kT * j;
+            if (q < xp) {
+                const int t = q >> lpr;
+                *(u32x4*)(smem + t * p.xpitch + 16 * (q - (t << lpr))) = XP[j];
+            }
+        }
+    }
+    __syncthreads();
+    GroupA A[4];
     {
         // token r; rows of A past M read token 0 and feed unwritten outputs
-        const uint16_t* xrow = p.x + (int64_t)(r < p.M ? r : 0) * p.K;
+        const unsigned char* xs = smem + (r < p.M ? r : 0) * p.xpitch;
+        const AMask mk = a_masks(c);
+        const uint32_t sh = 2u * (uint32_t)(c & 1);    // the lane's first element is odd when c is
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_group_x(xrow, 4 * ks + i, c, XR[i]);
+        for (int i = 0; i < 4; ++i) {
+            uint32_t X[10];
+            load_group_x(xs, 4 * ks + i, c, X);
+            A[i] = build_group_a(X, sh, mk);
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();                                  // the staged activations are read
     fill_book(lut, tid);
 
     // LDS destination of the piece in a tile: row-padded code rows, then
@@ -182,13 +215,6 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
             const int row = (int)piece / spr;
             dst = (uint32_t)((sbr * p.pitch) + row * p.spitch + 16 * ((int)piece - row * spr));
         }
-    }
-    GroupA A[4];
-    {
-        const AMask mk = a_masks(c);
-        const uint32_t sh = 2u * (uint32_t)(c & 1);    // the lane's first element is odd when c is
-#pragma unroll
-        for (int i = 0; i < 4; ++i) A[i] = build_group_a(XR[i], sh, mk);
     }
     const uint32_t cofs = (uint32_t)(lane & 31) << 3;    // code-book copy lane % 32
 
@@ -322,6 +348,9 @@ bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.pitch = 4 * pd;
     p.spitch = 4 * ((int)ng / 2 + 2);
     p.lnks = ng == 16 ? 2 : ng == 32 ? 3 : 4;
+    p.lxpr = p.lnks + 5;                         // K / 8 = 32 * 4-group slices
+    p.xpitch = 2 * (int)a.K + 16;
+    if (a.M * p.xpitch > kBookBytes + 2 * kTileBytes + 2 * kRedBytes) return false;
     const int nrs = kW >> p.lnks;
     if (16 * nrs * (p.pitch + p.spitch) > kTileBytes) return false;
     // lanes per output: the outputs of a super-block (M x 16 nrs) times the
