@@ -51,8 +51,6 @@ struct BatchParams {
     int ng, M;
     const uint8_t* codes;
     const uint16_t* scales;
-    uint32_t code_bytes;         // N * ng * 13
-    uint32_t scale_bytes;        // N * ng * 2
     int pitch, spitch;           // LDS bytes of a code / scale row of a tile
     int lnks;                    // log2 of the 4-group slices of K
     int lT;                      // log2 of the lanes that add up one output
@@ -146,21 +144,31 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     const uint32_t sbs = (uint32_t)p.ng << (lsbr + 1);   // scale bytes (2048)
 
     // ---- thread tid moves piece tid of a super-block: code pieces first
-    // (sbb / 16 of them), then scale pieces; the address is clamped into the
-    // arrays (rows past N are loaded from the end and never written out)
+    // (sbb / 16 of them), then scale pieces.  Rows past the workgroup's last
+    // row (and super-blocks past its last one) read its last row again, a
+    // cache hit, so that no launch fetches a neighbour's rows from HBM.
     const int ncp = (int)(sbb >> 4);
     const bool is_code = tid < ncp;
     const int sp = tid - ncp;                         // scale piece when >= 0
     const bool stores = is_code || sp < (int)(sbs >> 4);
     const uint8_t* src = is_code ? p.codes : (const uint8_t*)p.scales;
-    const uint32_t src_end = is_code ? p.code_bytes : p.scale_bytes;
-    const uint32_t src_sb = is_code ? sbb : sbs;
-    const uint32_t piece = (uint32_t)(is_code ? tid : (stores ? sp : 0));
-    const uint32_t src_wg = (uint32_t)r0 * (src_sb >> lsbr);   // first byte of the workgroup
+    int prow, pcol;                                   // row and byte of the piece in the super-block
+    {
+        const int ppr = is_code ? (int)(rb >> 4) : (p.ng >> 3);   // 16-byte pieces of a row
+        const int piece = is_code ? tid : (stores ? sp : 0);
+        prow = piece / ppr;
+        pcol = 16 * (piece - prow * ppr);
+    }
+    const uint32_t rowb = is_code ? rb : 2u * (uint32_t)p.ng;   // bytes of a row
     auto load_sb = [&](int k) {
-        const uint32_t o = min(src_wg + (uint32_t)k * src_sb + 16u * piece, src_end - 16u);
+        const int row = min((k << lsbr) + prow, nrows - 1);
+        const uint32_t o = (uint32_t)(r0 + row) * rowb + (uint32_t)pcol;
         return __builtin_nontemporal_load((const u32x4a*)(src + o));
     };
+    // LDS destination of the piece in a tile: row-padded code rows, then
+    // row-padded scale rows (conflict-free reads)
+    const uint32_t dst = is_code ? (uint32_t)(prow * p.pitch + pcol)
+                                 : (uint32_t)(sbr * p.pitch + prow * p.spitch + pcol);
     u32x4 R0 = load_sb(0), R1 = load_sb(1);
 
     // ---- activations: x goes through LDS (the whole shared space, before
@@ -203,19 +211,6 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     __syncthreads();                                  // the staged activations are read
     fill_book(lut, tid);
 
-    // LDS destination of the piece in a tile: row-padded code rows, then
-    // row-padded scale rows (conflict-free reads)
-    uint32_t dst;
-    {
-        const int cpr = (int)(rb >> 4), spr = p.ng >> 3;   // 16-byte pieces of a row
-        if (is_code) {
-            const int row = tid / cpr;
-            dst = (uint32_t)(row * p.pitch + 16 * (tid - row * cpr));
-        } else {
-            const int row = (int)piece / spr;
-            dst = (uint32_t)((sbr * p.pitch) + row * p.spitch + 16 * ((int)piece - row * spr));
-        }
-    }
     const uint32_t cofs = (uint32_t)(lane & 31) << 3;    // code-book copy lane % 32
 
     // ---- reduction of super-block k by every thread: output (m, n) takes
@@ -337,8 +332,6 @@ bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.M = (int)a.M;
     p.codes = a.codes[0];
     p.scales = a.scales[0];
-    p.code_bytes = (uint32_t)(a.N * ng * kNB);
-    p.scale_bytes = (uint32_t)(a.N * ng * 2);
     // code rows: a multiple of 16 bytes, at least 4 past the row, and
     // pitch / 4 == 4 (mod 8) so that 16 rows start in distinct bank quads;
     // scale rows: pitch / 4 == 2 (mod 4) for 8-byte reads of 16 rows
