@@ -172,6 +172,19 @@ inline int64_t tq_prefill_ws_bytes(int64_t M, int64_t K) {
     return tq_prefill_ws_flags_offset(M, K) + (M + 127) / 128 * ((K + 63) / 64) * 4;
 }
 
+// Compute units of the current device (256 when the query fails), read once;
+// kernels that place one workgroup per compute unit size their grids by it.
+inline int compute_unit_count() {
+    static const int cus = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            return v;
+        return 256;
+    }();
+    return cus;
+}
+
 hipError_t launch_tq_matmul(const TqMatmulArgs& a, hipStream_t s);
 // Streaming form for a few tokens (dense M <= 4, or <= 16 when the codes stay
 // in LDS; grouped experts); false when the call is outside its domain.

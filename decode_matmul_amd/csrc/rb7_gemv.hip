@@ -43,10 +43,7 @@ constexpr int kTileRowBytes = kTileK * 7 / 8;     // 448
 constexpr int kPieces = kTileRowBytes / 16;       // 28
 constexpr int kPitch = kTileRowBytes + 16;        // LDS bytes per tile row
 constexpr int kTileBytes = 16 * kPitch;
-constexpr int kCopies = 16;
-constexpr int kLutBytes = 128 * 4 * kCopies;
-static_assert(2 * kTileBytes >= kWaves * 64 * 4 * 4, "reduction fits the tile buffers");
-static_assert(kThreads == 4 * 128, "four threads per code-book entry");
+static_assert(2 * kTileBytes >= kWaves * 64 * 4 * 4, "a block's reduction fits two tile buffers");
 
 constexpr int kPlainThreads = 256;                // plain kernel: 4 waves, 16 rows
 
@@ -73,14 +70,15 @@ __device__ __forceinline__ float index_value(const Params& p, const float* table
     return c < 243 ? v : 0.f;
 }
 
-// LDS byte address 64 * index + lane_off of index i (constant after
-// unrolling) of indices held at bits 7 i of F.
+// LDS byte address (index << SH) + lane_off of index i (constant after
+// unrolling) of indices held at bits 7 i of F; SH = log2 of an entry's bytes.
+template <int SH>
 __device__ __forceinline__ uint32_t index_addr(const uint32_t* F, int i, uint32_t lane_off) {
     const int bit = 7 * i, d = bit >> 5, o = bit & 31;
     uint32_t v;
-    if (o + 7 <= 32) v = o >= 6 ? F[d] >> (o - 6) : F[d] << (6 - o);
-    else v = __builtin_amdgcn_alignbit(F[d + 1], F[d], (uint32_t)(o - 6));
-    return (v & 0x1fc0u) | lane_off;
+    if (o + 7 <= 32) v = o >= SH ? F[d] >> (o - SH) : F[d] << (SH - o);
+    else v = __builtin_amdgcn_alignbit(F[d + 1], F[d], (uint32_t)(o - SH));
+    return (v & (0x7fu << SH)) | lane_off;
 }
 
 __device__ __forceinline__ void epilogue(const Params& p, int64_t n, int m, float v) {
@@ -94,15 +92,28 @@ __device__ __forceinline__ void epilogue(const Params& p, int64_t n, int m, floa
     else ((uint16_t*)p.y)[idx] = f32_to_bf16_rne(v);
 }
 
-__global__ void __launch_bounds__(kThreads, 2)
+// NB = 2: a workgroup of 16 waves owns two adjacent 16-row blocks (8 waves
+// each, one code book, one barrier per tile for all 16), as in the byte-code
+// kernel: two 8-wave workgroups on one compute unit drift apart, one keeps
+// both blocks in step.  Its code book has 64 copies (every lane its own
+// bank); the 8-wave form keeps 16.
+template <int NB>
+__global__ void __launch_bounds__(kThreads * NB, 2 / NB)
 rb7_gemv_tiled_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) unsigned char lut[kLutBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char tiles[2][kTileBytes];
+    constexpr int kCopies = NB == 2 ? 64 : 16;
+    constexpr int kEntryShift = NB == 2 ? 8 : 6;           // log2(4 kCopies)
+    constexpr int kPerEntry = kThreads * NB / 128;         // threads filling one entry
+    __shared__ __attribute__((aligned(16))) unsigned char lut[128 * 4 * kCopies];
+    // tile t of block b in tiles[NB (t & 1) + b]; after the loop block b's
+    // partial sums take tiles[2 b] and tiles[2 b + 1]
+    __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * NB][kTileBytes];
 
     const int tid = threadIdx.x;
-    const int wave = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
+    const int wave_all = readfirstlane(tid >> 6);   // wave-uniform: scalar loop bounds
+    const int blk = wave_all / kWaves;              // row block of this wave
+    const int wave = wave_all % kWaves;             // its role in the block
     const int lane = tid & 63;
-    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * 16;
+    const int64_t row0 = (xcd_block(blockIdx.x, gridDim.x) * NB + blk) * 16;
     const int64_t ntiles = p.K / kTileK;          // >= 1: the launcher requires K >= kTileK
 
     // fetch: piece (lane % 28) of tile row 2 wave + lane / 28 (lanes 56..63
@@ -137,22 +148,25 @@ rb7_gemv_tiled_kernel(Params p) {
 
     // the list entry is read ahead of the tiles; the book entry it names is
     // read behind them (waiting for it waits for the first two tiles too)
-    const int lj = tid >> 2;                                   // code-book entry 0..127
+    const int lj = tid / kPerEntry;                            // code-book entry 0..127
     const uint32_t uc = p.used[lj];
     Stage s0, s1;
     fetch(0, s0);
     fetch(1, s1);
-    {   // entry lj, copies 4 (tid & 3) .. + 3
-        const float* table = rb_table_of(p.table, p.table_rows, row0);
+    {   // entry lj, copies (kCopies / kPerEntry) (tid % kPerEntry) .. (the book
+        // of the workgroup's first row: both blocks share it)
+        const float* table = rb_table_of(p.table, p.table_rows, row0 - 16 * blk);
         const float tv = table[uc < 243 ? uc : 0];
         const uint32_t e = split_bf16_pair(uc < 243 ? tv : 0.f);
-        *(u32x4*)(lut + lj * 4 * kCopies + (tid & 3) * 16) = u32x4{e, e, e, e};
+        unsigned char* base = lut + lj * 4 * kCopies + (tid % kPerEntry) * 4 * (kCopies / kPerEntry);
+#pragma unroll
+        for (int i = 0; i < kCopies / kPerEntry / 4; ++i) *(u32x4*)(base + 16 * i) = u32x4{e, e, e, e};
     }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // copy (lane % 16); the empty asm hides its known bits, so that each
+    // copy (lane % kCopies); the empty asm hides its known bits, so that each
     // address stays one and-or rather than an and plus an add
-    uint32_t lane_off = (uint32_t)(lane & 15) << 2;
+    uint32_t lane_off = (uint32_t)(lane & (kCopies - 1)) << 2;
     asm volatile("" : "+v"(lane_off));
 
     // tile t goes to LDS buffer t & 1: the barrier after writing tile t also
@@ -160,7 +174,7 @@ rb7_gemv_tiled_kernel(Params p) {
     auto step = [&](const Stage& S, int buf) {
         // keep the next stage's work (it waits on younger loads) out of this step
         __builtin_amdgcn_sched_barrier(0);
-        unsigned char* tile = tiles[buf];
+        unsigned char* tile = tiles[NB * buf + blk];
         if (writer) *(u32x4*)(tile + lrow * kPitch + 16 * lpiece) = S.c;
         __syncthreads();
         const uint32_t* r = (const uint32_t*)(tile + col * kPitch) + rd0;
@@ -179,7 +193,8 @@ rb7_gemv_tiled_kernel(Params p) {
             aq[2] = perm_b32(x23, x23, 0x01000100u);
             aq[3] = perm_b32(x23, x23, 0x03020302u);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bq[i] = *(const uint32_t*)(lut + index_addr(F, 4 * j + i, lane_off));
+            for (int i = 0; i < 4; ++i)
+                bq[i] = *(const uint32_t*)(lut + index_addr<kEntryShift>(F, 4 * j + i, lane_off));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aq),
                                                           __builtin_bit_cast(bf16x8, bq), acc,
                                                           0, 0, 0);
@@ -195,10 +210,10 @@ rb7_gemv_tiled_kernel(Params p) {
     }
     if (t < ntiles) step(s0, 0);
 
-    // partials of the 8 waves meet in the (now idle) tile buffers; C[4 (lane
-    // >> 4) + i][lane & 15] is token 4 (lane >> 4) + i, row lane & 15
+    // partials of a block's 8 waves meet in two (now idle) tile buffers;
+    // C[4 (lane >> 4) + i][lane & 15] is token 4 (lane >> 4) + i, row lane & 15
     __syncthreads();
-    float* red = (float*)tiles[0];                                // [kWaves][64][4]
+    float* red = (float*)tiles[2 * blk];                          // [kWaves][64][4]
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
     __syncthreads();
@@ -282,9 +297,17 @@ hipError_t launch_rb7_gemv(const RbMatmulArgs& a, hipStream_t s) {
     // whole tiles and 16-byte aligned rows (7 K / 8 is then a multiple of 448)
     const bool tiled = a.K >= kTileK && (a.K % kTileK == 0) &&
                        (((uintptr_t)a.codes & 15) == 0) && (((uintptr_t)a.x & 3) == 0);
-    if (tiled)
-        hipLaunchKernelGGL(rb7_gemv_tiled_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-    else
+    if (tiled) {
+        // two row blocks a workgroup when that still gives every compute unit
+        // one, and both blocks use one code book
+        const bool pair = blocks >= 2 * (int64_t)compute_unit_count() &&
+                          (a.table_rows == 0 || a.table_rows % 32 == 0);
+        if (pair)
+            hipLaunchKernelGGL(rb7_gemv_tiled_kernel<2>, dim3((unsigned)((blocks + 1) / 2)),
+                               dim3(2 * kThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL(rb7_gemv_tiled_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    } else
         hipLaunchKernelGGL(rb7_gemv_plain_kernel, dim3((unsigned)blocks), dim3(kPlainThreads), 0,
                            s, p);
     return hipGetLastError();

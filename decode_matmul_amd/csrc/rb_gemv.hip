@@ -487,19 +487,6 @@ rb_gemv_tiled_kernel(Params p) {
     }
 }
 
-int rb_compute_units() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
 }  // namespace
 
 hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
@@ -533,7 +520,7 @@ hipError_t launch_rb_gemv(const RbMatmulArgs& a, hipStream_t s) {
         // two row blocks a workgroup when that still gives every compute unit
         // one, and both blocks use one code book
         const int64_t nblk = (a.N + 15) / 16;
-        const bool pair = nblk >= 2 * (int64_t)rb_compute_units() &&
+        const bool pair = nblk >= 2 * (int64_t)compute_unit_count() &&
                           (a.table_rows == 0 || a.table_rows % 32 == 0);
         const dim3 g1((unsigned)nblk), g2((unsigned)((nblk + 1) / 2));
         if (a.M >= kXStageMinM) {

@@ -299,20 +299,6 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     reduce(nsb - 1);
 }
 
-int batch_compute_units() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
 }  // namespace
 
 bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
@@ -350,7 +336,7 @@ bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     // lanes fit the workgroup, at most 4 and at most the slices
     const int outs = (int)a.M * 16 * nrs;
     p.lT = outs * 4 <= kT ? 2 : outs * 2 <= kT ? 1 : 0;
-    const int cus = batch_compute_units();
+    const int cus = compute_unit_count();
     const int64_t rpw = (a.N + cus - 1) / cus;
     p.rows_per_wg = (int)rpw;
     p.y = a.y;

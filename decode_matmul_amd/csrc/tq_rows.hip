@@ -560,20 +560,6 @@ __global__ void __launch_bounds__(kT, 1) tq_rows_hot_kernel(RowsParams ph, RowsP
 constexpr int kMaxBlocks = 8;
 constexpr int kLdsLimit = 160 * 1024;
 
-int compute_units() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
 }  // namespace
 
 // Streaming ternary GEMV; returns false (launching nothing) when the call is
@@ -616,7 +602,7 @@ static bool rows_setup(const TqMatmulArgs& a, RowsParams& p, size_t& smem_out, i
     if (grouped) {
         rpw = std::min<int64_t>(16 * kMaxBlocks, (a.N + 7) & ~(int64_t)7);
     } else {
-        const int cus = compute_units();
+        const int cus = compute_unit_count();
         rpw = (a.N + cus - 1) / cus;
         rpw = (rpw + 7) & ~(int64_t)7;
         if (rpw > 16 * kMaxBlocks) rpw = 16 * kMaxBlocks;

@@ -567,20 +567,6 @@ __global__ void __launch_bounds__(kT, 1) tq_wave_hot_kernel(WaveParams hot, Wave
     grouped_work<1>(cold, lut, xs, meta, red, false);
 }
 
-int wave_compute_units() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
 }  // namespace
 
 // Parameters of a call in the wave form's domain: dense calls with
@@ -606,7 +592,7 @@ static bool wave_setup(const TqMatmulArgs& a, WaveParams& p, size_t& smem) {
     }
     const int ng = (int)(a.K / 64);
     const int nkq = ng / 16, nrr = kW / nkq;
-    const int cus = wave_compute_units();
+    const int cus = compute_unit_count();
     p.x = a.x;
     p.K = a.K;
     p.N = a.N;

@@ -285,6 +285,22 @@ def test_rb_matmul7_shapes(dmm, M, N, K):
             bias=True, n_codes=128)
 
 
+# the two-block form (16 waves on two 16-row blocks, taken when the row
+# blocks are at least twice the compute units): an odd block count (the last
+# workgroup's second block lies past N), N ending inside a block, one book,
+# 32- and 64-row books (both blocks share one), and a row count just below
+# the two-block form
+M7_PAIR_CASES = [(1, 8208, 512, 0), (3, 8208, 1024, 32), (16, 8200, 512, 0), (4, 8192, 1024, 64),
+                 (2, 8000, 512, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,table_rows", M7_PAIR_CASES)
+def test_rb_matmul7_two_blocks(dmm, M, N, K, table_rows):
+    m7_case(dmm, M, N, K, seed=M + N + 7 * K + table_rows, table_rows=table_rows)
+    m7_case(dmm, M, N, K, seed=2 * M + N + K, table_rows=table_rows, ydt=torch.bfloat16,
+            rho_rows=1, bias=True, n_codes=128)
+
+
 def test_rb_matmul7_offsets_heads_and_list_entries(dmm):
     """Unaligned index rows and activations, head-block scales, and a list
     whose unused entries hold arbitrary bytes (index 0 names code 250)."""
