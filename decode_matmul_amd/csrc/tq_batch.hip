@@ -34,8 +34,10 @@ namespace {
 constexpr int kW = 16;
 constexpr int kT = 64 * kW;
 constexpr int kNB = 13;                  // code bytes per group of 64 trits
-constexpr int kPart = 64 * 4 + 4;        // floats of one wave's partial sums (+4: the slices
-                                         // a lane group adds sit in distinct banks)
+// floats of one wave's partial sums, stored value-major ([4][64]: value v of
+// lane l at 64 v + l); the 16 padding floats put the slices that a lane
+// group adds 16 banks apart, so a wave's 64 reads hit 64 distinct banks
+constexpr int kPart = 64 * 4 + 16;
 constexpr int kTileBytes = 17920;        // code + scale tile of a super-block, largest K
 constexpr int kBookBytes = 256 * 256;    // code book: 256 entries x 32 copies x 8 bytes
 constexpr int kRedBytes = kW * kPart * 4;  // partial sums of a super-block
@@ -169,13 +171,13 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     // row-padded scale rows (conflict-free reads)
     const uint32_t dst = is_code ? (uint32_t)(prow * p.pitch + pcol)
                                  : (uint32_t)(sbr * p.pitch + prow * p.spitch + pcol);
-    u32x4 R0 = load_sb(0), R1 = load_sb(1);
-
     // ---- activations: x goes through LDS (the whole shared space, before
     // the code book is filled), loaded as coalesced 16-byte pieces; token
     // rows are padded by 16 bytes so that the 16 tokens fall in distinct
-    // banks.  Memory counters retire in order: the first super-blocks went
-    // out ahead of the pieces.
+    // banks.  The pieces go out first and the first two super-blocks right
+    // behind them: memory counters retire in order, so waiting for x does not
+    // wait for the code stream.
+    u32x4 R0, R1;
     {
         const int lpr = p.lxpr;                       // log2 of the 16-byte pieces of a row
         const int xp = p.M << lpr;
@@ -185,6 +187,8 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
             const int q = min(tid + kT * j, xp - 1);
             XP[j] = *(const u32x4a*)(p.x + 8 * (int64_t)q);
         }
+        R0 = load_sb(0);
+        R1 = load_sb(1);
 #pragma unroll
         for (int j = 0; j < kXPieces; ++j) {
             const int q = tid + kT * j;
@@ -213,31 +217,36 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
 
     const uint32_t cofs = (uint32_t)(lane & 31) << 3;    // code-book copy lane % 32
 
-    // ---- reduction of super-block k by every thread: output (m, n) takes
-    // lanes q = tid & (T - 1) of a group of T, which add slices q, q + T, ...
-    // and then sum across the group in a fixed order
+    // ---- reduction of super-block k by every thread: output (m, n) of the
+    // super-block takes lanes q = tid & (T - 1) of a group of T, which add
+    // slices q, q + T, ... (at most four a lane: nks / T <= 4 for every K
+    // and M) and then sum across the group in a fixed order.  T is chosen so
+    // that one pass covers the super-block, so every index is set up once.
     const int lT = p.lT, T = 1 << lT;
+    const int rq = tid & (T - 1);
+    const int ro = tid >> lT;                         // output of this lane group
+    const int rn = ro & (sbr - 1), rm = ro >> lsbr;
+    const bool rvalid = rm < p.M && rq == 0;
+    const int rsrc = ((rn >> 4) << lnks) * kPart + 64 * (rm & 3) + 16 * ((rm & 15) >> 2) + (rn & 15);
+    const uint32_t ry = (uint32_t)min(rm, p.M - 1) * (uint32_t)p.N + (uint32_t)rn;   // y index less r0 and the super-block
     auto reduce = [&](int k) {
-        const float* rk = red + (k & 1) * kW * kPart;
-        const int rows = min(sbr, nrows - (k << lsbr));
-        const int q = tid & (T - 1);
-        for (int o0 = 0; o0 < (p.M << lsbr); o0 += kT >> lT) {
-            const int o = o0 + (tid >> lT);
-            const int n = o & (sbr - 1), m = o >> lsbr;
-            float sum = 0.f;
-            if (m < p.M) {
-                const float* src_p = rk + ((n >> 4) << lnks) * kPart + 4 * (16 * (m >> 2) + (n & 15)) + (m & 3);
-                for (int w = q; w < nks; w += T) sum += src_p[w * kPart];
-            }
-            // groups of T consecutive lanes: pairwise in a fixed order
-            if (T >= 2) sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, true));
-            if (T >= 4) sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, true));
-            if (q == 0 && m < p.M && n < rows) {
-                const float v = 0.5f * sum;           // the code book holds 2t
-                const int64_t yi = (int64_t)m * p.N + r0 + ((int64_t)k << lsbr) + n;
-                if (p.y_dtype == TQ_F32) ((float*)p.y)[yi] = v;
-                else ((uint16_t*)p.y)[yi] = f32_to_bf16_rne(v);
-            }
+        const float* src_p = red + (k & 1) * kW * kPart + rsrc;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int w = rq + (j << lT);             // (read clamped into the slices)
+            const float r = src_p[min(w, nks - 1) * kPart];
+            v[j] = w < nks ? r : 0.f;
+        }
+        float sum = (v[0] + v[1]) + (v[2] + v[3]);
+        // groups of T consecutive lanes: pairwise in a fixed order
+        if (T >= 2) sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, true));
+        if (T >= 4) sum += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, true));
+        if (rvalid && rn < nrows - (k << lsbr)) {
+            const float r = 0.5f * sum;               // the code book holds 2t
+            const uint32_t yi = ry + (uint32_t)(r0 + (k << lsbr));
+            if (p.y_dtype == TQ_F32) ((float*)p.y)[yi] = r;
+            else ((uint16_t*)p.y)[yi] = f32_to_bf16_rne(r);
         }
     };
 
@@ -259,33 +268,54 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
             const unsigned char* trow = tile + ((rs << 4) + r) * p.pitch;
             const unsigned char* srow = tile + (sbr * p.pitch) + ((rs << 4) + r) * p.spitch;
             const u32x2 S = *(const u32x2*)(srow + 8 * ks);
-            f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+            // the four groups in phases (code words, lookups, then the three
+            // MFMAs of every group in turn), so that the groups' MFMA chains
+            // interleave instead of waiting on each other
+            uint32_t W[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t byte = (uint32_t)(kNB * (4 * ks + i) + 3 * c);
                 const u32x2 d = *(const u32x2a*)(trow + (byte & ~3u));
-                const uint32_t W = align_bytes(d.y, d.x, byte & 3u);
-                const uint2 e0 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0400u));
-                const uint2 e1 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0500u));
-                const uint2 e2 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0600u));
-                const uint2 e3 = *(const uint2*)(lut + perm_b32(W, cofs, 0x0c0c0700u));
-                f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, A[i].a0), __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y}),
+                W[i] = align_bytes(d.y, d.x, byte & 3u);
+            }
+            uint2 e[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    e[i][j] = *(const uint2*)(lut + perm_b32(W[i], cofs, 0x0c0c0400u + ((uint32_t)j << 8)));
+            f32x4 acc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, A[i].a0),
+                    __builtin_bit_cast(bf16x8, u32x4{e[i][0].x, e[i][0].y, e[i][1].x, e[i][1].y}),
                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, A[i].a1), __builtin_bit_cast(bf16x8, u32x4{e2.x, e2.y, e3.x, e3.y}),
-                    acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, A[i].a1),
+                    __builtin_bit_cast(bf16x8, u32x4{e[i][2].x, e[i][2].y, e[i][3].x, e[i][3].y}),
+                    acc[i], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
                 // digit 4 of bytes (0, 2) and (1, 3)
-                const u32x2 q = {t4pair(W & 0x00FF00FFu), t4pair(perm_b32(W, W, 0x0c030c01u))};
-                acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, A[i].a2),
-                                                                __builtin_bit_cast(bf16x4, q), acc, 0, 0, 0);
+                const u32x2 q = {t4pair(W[i] & 0x00FF00FFu), t4pair(perm_b32(W[i], W[i], 0x0c030c01u))};
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, A[i].a2),
+                                                                   __builtin_bit_cast(bf16x4, q), acc[i], 0, 0, 0);
+            }
+            f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
                 const uint32_t sw = (i < 2 ? S.x : S.y) >> (16 * (i & 1));
                 const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sw);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) tot[v] = __builtin_fmaf(sc, acc[v], tot[v]);
+                for (int v = 0; v < 4; ++v) tot[v] = __builtin_fmaf(sc, acc[i][v], tot[v]);
             }
-            // D[4 c + v][r]: tokens 4c .. 4c+3 of row r of the block
-            *(f32x4*)(red + ((k & 1) * kW + wave) * kPart + 4 * lane) = tot;
+            // D[4 c + v][r]: token 4c + v of row r of the block, value-major
+            float* dst_p = red + ((k & 1) * kW + wave) * kPart + lane;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dst_p[64 * v] = tot[v];
         }
     };
     // two steps a trip, so that super-blocks k and k + 1 stay in their own
