@@ -41,7 +41,8 @@ constexpr int kPart = 64 * 4 + 16;
 constexpr int kTileBytes = 17920;        // code + scale tile of a super-block, largest K
 constexpr int kBookBytes = 256 * 256;    // code book: 256 entries x 32 copies x 8 bytes
 constexpr int kRedBytes = kW * kPart * 4;  // partial sums of a super-block
-constexpr int kXPieces = 8;              // 16-byte pieces of x per thread: 16 tokens x 4096
+constexpr int kXPieces = 8;              // staged x: 16-byte pieces per thread (16 tokens x 4096)
+constexpr int kXStageMinM = 9;           // activations staged in LDS from this many tokens
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -56,8 +57,8 @@ struct BatchParams {
     int pitch, spitch;           // LDS bytes of a code / scale row of a tile
     int lnks;                    // log2 of the 4-group slices of K
     int lT;                      // log2 of the lanes that add up one output
-    int lxpr;                    // log2 of the 16-byte pieces of a row of x
-    int xpitch;                  // LDS bytes of a staged row of x
+    int lxpr;                    // staged x: log2 of the 16-byte pieces of a row
+    int xpitch;                  // staged x: LDS bytes of a row
     int rows_per_wg;
     void* y;
     int y_dtype;
@@ -71,8 +72,18 @@ struct GroupA {
 
 // Activations of lane (c, t) for group g: elements 64 g + 15 c .. + 18 of
 // token t's row, as the ten dwords from the even element at or below the
-// first (all inside the group), read from the row staged in LDS at xs.
-__device__ __forceinline__ void load_group_x(const unsigned char* xs, int g, int c, uint32_t (&X)[10]) {
+// first (all inside the group), from the row in memory ...
+__device__ __forceinline__ void load_group_x(const uint16_t* xrow, int g, int c, uint32_t (&X)[10]) {
+    const uint16_t* p = xrow + ((64 * g + 15 * c) & ~1);
+    const u32x4 v0 = *(const u32x4a*)(p), v1 = *(const u32x4a*)(p + 8);
+    const u32x2 v2 = *(const u32x2a*)(p + 16);
+    X[0] = v0.x; X[1] = v0.y; X[2] = v0.z; X[3] = v0.w;
+    X[4] = v1.x; X[5] = v1.y; X[6] = v1.z; X[7] = v1.w;
+    X[8] = v2.x; X[9] = v2.y;
+}
+
+// ... or from the row staged in LDS at xs.
+__device__ __forceinline__ void lds_group_x(const unsigned char* xs, int g, int c, uint32_t (&X)[10]) {
     const unsigned char* p = xs + 2 * ((64 * g + 15 * c) & ~1);
 #pragma unroll
     for (int q = 0; q < 10; q += 2) {
@@ -122,6 +133,11 @@ __device__ __forceinline__ GroupA build_group_a(const uint32_t (&X)[10], uint32_
 // to an LDS tile; after one barrier wave (ks, rs) multiplies 16-row block rs
 // of it by the 4-group slice ks of K.  The slices' partial sums of a
 // super-block are added up after the next barrier, by all waves.
+// XS: the activations go through LDS (more than 8 tokens: every workgroup
+// reads all of x, and coalesced pieces cost less than per-lane windows of 16
+// token rows); otherwise each lane reads its windows directly, and the code
+// book is filled while they are in flight.
+template <bool XS>
 __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     // code book at LDS address 0 (a lookup address is one v_perm), then two
     // tiles and two sets of partial sums
@@ -171,15 +187,19 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     // row-padded scale rows (conflict-free reads)
     const uint32_t dst = is_code ? (uint32_t)(prow * p.pitch + pcol)
                                  : (uint32_t)(sbr * p.pitch + prow * p.spitch + pcol);
-    // ---- activations: x goes through LDS (the whole shared space, before
-    // the code book is filled), loaded as coalesced 16-byte pieces; token
-    // rows are padded by 16 bytes so that the 16 tokens fall in distinct
-    // banks.  The pieces go out first and the first two super-blocks right
-    // behind them: memory counters retire in order, so waiting for x does not
-    // wait for the code stream.
+    // ---- activations first and the first two super-blocks right behind them
+    // (memory counters retire in order, so waiting for x does not wait for
+    // the code stream).  Rows of A past M read token 0 and feed unwritten
+    // outputs.
     u32x4 R0, R1;
-    {
-        const int lpr = p.lxpr;                       // log2 of the 16-byte pieces of a row
+    GroupA A[4];
+    const AMask mk = a_masks(c);
+    const uint32_t xsh = 2u * (uint32_t)(c & 1);      // the lane's first element is odd when c is
+    if constexpr (XS) {
+        // x through LDS (the whole shared space, before the code book is
+        // filled) as coalesced 16-byte pieces; token rows are padded by 16
+        // bytes so that the 16 tokens fall in distinct banks
+        const int lpr = p.lxpr;
         const int xp = p.M << lpr;
         u32x4 XP[kXPieces];
 #pragma unroll
@@ -197,23 +217,28 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
                 *(u32x4*)(smem + t * p.xpitch + 16 * (q - (t << lpr))) = XP[j];
             }
         }
-    }
-    __syncthreads();
-    GroupA A[4];
-    {
-        // token r; rows of A past M read token 0 and feed unwritten outputs
+        __syncthreads();
         const unsigned char* xs = smem + (r < p.M ? r : 0) * p.xpitch;
-        const AMask mk = a_masks(c);
-        const uint32_t sh = 2u * (uint32_t)(c & 1);    // the lane's first element is odd when c is
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint32_t X[10];
-            load_group_x(xs, 4 * ks + i, c, X);
-            A[i] = build_group_a(X, sh, mk);
+            lds_group_x(xs, 4 * ks + i, c, X);
+            A[i] = build_group_a(X, xsh, mk);
         }
+        __syncthreads();                              // the staged activations are read
+        fill_book(lut, tid);
+    } else {
+        uint32_t XR[4][10];
+        const uint16_t* xrow = p.x + (int64_t)(r < p.M ? r : 0) * p.K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_group_x(xrow, 4 * ks + i, c, XR[i]);
+        R0 = load_sb(0);
+        R1 = load_sb(1);
+        __builtin_amdgcn_sched_barrier(0);
+        fill_book(lut, tid);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[i] = build_group_a(XR[i], xsh, mk);
     }
-    __syncthreads();                                  // the staged activations are read
-    fill_book(lut, tid);
 
     const uint32_t cofs = (uint32_t)(lane & 31) << 3;    // code-book copy lane % 32
 
@@ -359,7 +384,8 @@ bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.lnks = ng == 16 ? 2 : ng == 32 ? 3 : 4;
     p.lxpr = p.lnks + 5;                         // K / 8 = 32 * 4-group slices
     p.xpitch = 2 * (int)a.K + 16;
-    if (a.M * p.xpitch > kBookBytes + 2 * kTileBytes + 2 * kRedBytes) return false;
+    const bool xs = a.M >= kXStageMinM;
+    if (xs && a.M * p.xpitch > kBookBytes + 2 * kTileBytes + 2 * kRedBytes) return false;
     const int nrs = kW >> p.lnks;
     if (16 * nrs * (p.pitch + p.spitch) > kTileBytes) return false;
     // lanes per output: the outputs of a super-block (M x 16 nrs) times the
@@ -372,7 +398,8 @@ bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.y = a.y;
     p.y_dtype = a.y_dtype;
     const int64_t wgs = (a.N + rpw - 1) / rpw;
-    hipLaunchKernelGGL(tq_batch_kernel, dim3((unsigned)wgs), dim3(kT), 0, s, p);
+    if (xs) hipLaunchKernelGGL(tq_batch_kernel<true>, dim3((unsigned)wgs), dim3(kT), 0, s, p);
+    else hipLaunchKernelGGL(tq_batch_kernel<false>, dim3((unsigned)wgs), dim3(kT), 0, s, p);
     *err = hipGetLastError();
     return true;
 }
