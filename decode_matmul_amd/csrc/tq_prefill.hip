@@ -28,15 +28,16 @@
 //    K-step's fragments are read and slice s + 2 (loaded from global memory
 //    an iteration earlier) is decoded into the buffer slice s has just
 //    vacated.  One barrier per slice.
-//  * Decode: thread t owns tile row t % 256 and the 16 trits 16 u .. 16 u + 15
-//    of the group, u = 2 h + t / 256 (h the slice's half; t / 256 is
-//    wave-uniform).  They are base-3 digits u .. u + 15 of the four code
-//    bytes 3 u .. 3 u + 3 read as one digit stream (byte i, digit d at
-//    position 5 i + d).  Each byte is looked up in a 16-copy table of its five
-//    digits' fp16 high bytes; the 20 stream bytes are packed into five words
-//    and each fp16 pair of t is one v_perm with a wave-uniform selector, so
-//    every (half, u) takes the same instructions.  One packed fp16 multiply
-//    by (s, s) per pair gives the weights.
+//  * Decode: lanes 2 r and 2 r + 1 of wave w own tile row 32 w + r (so one
+//    load instruction touches 32 rows' lines, not 64) and the 16 trits
+//    16 u .. 16 u + 15 of the group, u = 2 h + (lane & 1) (h the slice's
+//    half).  They are base-3 digits u .. u + 15 of the four code bytes
+//    3 u .. 3 u + 3 read as one digit stream (byte i, digit d at position
+//    5 i + d).  Each byte is looked up in a 16-copy table of its five digits'
+//    fp16 high bytes; the 20 stream bytes are packed into five words and each
+//    fp16 pair of t is one v_perm, so every (half, u) takes the same
+//    instructions.  One packed fp16 multiply by (s, s) per pair gives the
+//    weights.
 //  * Tile rows are 80 bytes apart, so the 8 lanes of a 16-byte column read
 //    cover distinct banks.
 #include <type_traits>
@@ -121,7 +122,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     const int lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
     const int wm = wave / kWN, wn = wave % kWN;
-    const int jpart = wave >> 2;                                // which 16 trits of a half
+    const int jpart = lane & 1;                                 // which 16 trits of a half
 
     // ---- trit table: 16 copies; entries 243..255 decode to zero
     for (int i = tid; i < 256 * 16; i += kThreads) {
@@ -147,7 +148,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     // this thread's activation chunks (rows xr + 128 i, 8 values at column
     // 8 xc) and weight row
     const int xc = tid & 3, xr = tid >> 2;
-    const int wr = tid & 255;
+    const int wr = 32 * wave + (lane >> 1);                     // the two lanes of a row share its lines
     const int64_t wrow = min(n0 + wr, p.N - 1);
     const int64_t row_bytes = (int64_t)p.ng * kNB;
 
