@@ -33,7 +33,7 @@
 //    16 u .. 16 u + 15 of the group, u = 2 h + (lane & 1) (h the slice's
 //    half).  They are base-3 digits u .. u + 15 of the four code bytes
 //    3 u .. 3 u + 3 read as one digit stream (byte i, digit d at position
-//    5 i + d).  Each byte is looked up in a 16-copy table of its five digits'
+//    5 i + d).  Each byte is looked up in a 32-copy table of its five digits'
 //    fp16 high bytes; the 20 stream bytes are packed into five words and each
 //    fp16 pair of t is one v_perm, so every (half, u) takes the same
 //    instructions.  One packed fp16 multiply by (s, s) per pair gives the
@@ -56,7 +56,7 @@ constexpr int MT = 4, NT = 2;                  // 32x32 MFMA tiles per wave alon
 constexpr int kNB = 13;                        // code bytes per group
 constexpr int kPitch = 2 * BK + 16;            // bytes per LDS tile row
 constexpr int kTileBytes = BM * kPitch;        // one operand tile (BM == BN)
-constexpr int kLutBytes = 256 * 128;           // entry b, copy c at (b << 7) | (c << 3)
+constexpr int kLutBytes = 256 * 256;           // entry b, copy c at (b << 8) | (c << 3)
 constexpr int kMapSlices = 1536;               // slices tracked one by one
 constexpr int kFlagRows = 128;                 // rows per pre-pass flag block
 constexpr int kSmemBytes = kLutBytes + 4 * kTileBytes + 64 + 8 * (kMapSlices + 2);
@@ -124,9 +124,9 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     const int wm = wave / kWN, wn = wave % kWN;
     const int jpart = lane & 1;                                 // which 16 trits of a half
 
-    // ---- trit table: 16 copies; entries 243..255 decode to zero
-    for (int i = tid; i < 256 * 16; i += kThreads) {
-        const int b = i >> 4, c = i & 15;
+    // ---- trit table: 32 copies; entries 243..255 decode to zero
+    for (int i = tid; i < 256 * 32; i += kThreads) {
+        const int b = i >> 5, c = i & 31;
         uint32_t lo = 0, hi = 0;
         if (b < 243) {
             const int d0 = b % 3, d1 = (b / 3) % 3, d2 = (b / 9) % 3, d3 = (b / 27) % 3, d4 = b / 81;
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
                  (trit_f16_hi(d3) << 24);
             hi = trit_f16_hi(d4);
         }
-        *(uint2*)(lut + ((b << 7) | (c << 3))) = make_uint2(lo, hi);
+        *(uint2*)(lut + ((b << 8) | (c << 3))) = make_uint2(lo, hi);
     }
     if (tid == 0) redo_n = 0;
     for (int i = tid; i <= kMapSlices + 1; i += kThreads) bad_map[i] = 0ull;
@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int nslices = 2 * p.ng * p.planes;
     const int psh = p.planes == 2 ? 2 : 1;                      // slice -> group shift
-    const uint32_t cofs = (uint32_t)(lane & 15) << 4;           // >> 1 below: copy lane % 16
+    const uint32_t cofs = (uint32_t)(lane & 31) << 3;           // copy lane % 32
 
     // this thread's activation chunks (rows xr + 128 i, 8 values at column
     // 8 xc) and weight row
@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
         uint32_t x[4], y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t a = perm_b32(D, cofs, 0x0c0c0400u + ((uint32_t)i << 8)) >> 1;
+            const uint32_t a = perm_b32(D, cofs, 0x0c0c0400u + ((uint32_t)i << 8));
             const uint2 e = *(const uint2*)(lut + a);
             x[i] = e.x;
             y[i] = e.y;
