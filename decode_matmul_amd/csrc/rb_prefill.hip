@@ -72,7 +72,8 @@ constexpr int kSmemBytes = kLutBytes + 4 * kTileBytes + kWords + 8 * (kMapSlices
 static_assert(kSlots * 32 == BN, "one slot per 32 tile rows");
 static_assert(kSmemBytes <= 160 * 1024, "fits the LDS of a CU");
 static_assert(kThreads / 64 <= 8, "one flag byte per wave");
-static_assert(kMapSlices * 2 <= 2 * kTileBytes, "the slice list fits LDS buffer 1");
+static_assert(kMapSlices * 2 <= kTileBytes,
+              "the slice list fits the activation tile of LDS buffer 1 (its weight tile takes the lo weights of a replay)");
 static_assert(BM == BN, "square tiles share one pitch");
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));

@@ -61,7 +61,8 @@ constexpr int kMapSlices = 1536;               // slices tracked one by one
 constexpr int kFlagRows = 128;                 // rows per pre-pass flag block
 constexpr int kSmemBytes = kLutBytes + 4 * kTileBytes + 64 + 8 * (kMapSlices + 2);
 static_assert(kSmemBytes <= 160 * 1024, "LDS");
-static_assert(kMapSlices * 2 <= 2 * kTileBytes, "the slice list fits LDS buffer 1");
+static_assert(kMapSlices * 2 <= kTileBytes,
+              "the slice list fits the activation tile of LDS buffer 1 (its weight tile takes the lo weights of a replay)");
 static_assert(BM == BN && BM == 2 * kFlagRows, "square tiles; two flag blocks per row tile");
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -535,8 +536,8 @@ __global__ void __launch_bounds__(256) tq_xconv_kernel(const uint16_t* __restric
 }  // namespace
 
 // Dense ternary matmul for many tokens; false (nothing launched) outside its
-// domain: G = 64, M >= 128, x 16-byte and codes 4-byte aligned, a grid within
-// the launch limits.
+// domain: G = 64, M >= 128, K < 2^23, x 16-byte and codes 4-byte aligned, a
+// grid within the launch limits.
 bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     if (a.n_experts != 0 || a.G != G || a.M < kFlagRows || a.K < G || a.K % G != 0 ||
         ((uintptr_t)a.x & 15) != 0 || ((uintptr_t)a.codes[0] & 3) != 0 ||
@@ -545,6 +546,7 @@ bool launch_tq_prefill(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     if (a.planes == 2 && (((uintptr_t)a.codes[1] & 3) != 0 || ((uintptr_t)a.scales[1] & 1) != 0))
         return false;
     if (2 * (a.K / G) * a.planes >= (1ll << 30)) return false;        // slice count in an int
+    if (a.K >= (1ll << 23)) return false;             // 32-bit element offsets inside a 256-row tile
     const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
     const int64_t gyf = (a.M + kFlagRows - 1) / kFlagRows;            // pre-pass row blocks
     if (gx == 0 || gx >= (1ll << 31) || gyf >= 65536) return false;
