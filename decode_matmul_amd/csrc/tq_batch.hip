@@ -58,7 +58,6 @@ struct BatchParams {
     int lnks;                    // log2 of the 4-group slices of K
     int lT;                      // log2 of the lanes that add up one output
     int lxpr;                    // staged x: log2 of the 16-byte pieces of a row
-    int xpitch;                  // staged x: LDS bytes of a row
     int rows_per_wg;
     void* y;
     int y_dtype;
@@ -196,9 +195,10 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     const AMask mk = a_masks(c);
     const uint32_t xsh = 2u * (uint32_t)(c & 1);      // the lane's first element is odd when c is
     if constexpr (XS) {
-        // x through LDS (the whole shared space, before the code book is
-        // filled) as coalesced 16-byte pieces; token rows are padded by 16
-        // bytes so that the 16 tokens fall in distinct banks
+        // x through LDS as coalesced 16-byte pieces, one half of K at a time
+        // in the tiles' space, so that the code book is filled while the
+        // pieces are in flight.  Token rows are padded by 16 bytes so that
+        // the 16 tokens fall in distinct banks.
         const int lpr = p.lxpr;
         const int xp = p.M << lpr;
         u32x4 XP[kXPieces];
@@ -209,24 +209,37 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
         }
         R0 = load_sb(0);
         R1 = load_sb(1);
-#pragma unroll
-        for (int j = 0; j < kXPieces; ++j) {
-            const int q = tid + kT * j;
-            if (q < xp) {
-                const int t = q >> lpr;
-                *(u32x4*)(smem + t * p.xpitch + 16 * (q - (t << lpr))) = XP[j];
-            }
-        }
-        __syncthreads();
-        const unsigned char* xs = smem + (r < p.M ? r : 0) * p.xpitch;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t X[10];
-            lds_group_x(xs, 4 * ks + i, c, X);
-            A[i] = build_group_a(X, xsh, mk);
-        }
-        __syncthreads();                              // the staged activations are read
         fill_book(lut, tid);
+        // every piece of this thread lies in K half (tid >> (lpr - 1)) & 1
+        // (kT is a multiple of the pieces of a row); the waves of slices
+        // ks < nks / 2 read half 0
+        const int hb = lpr - 1;
+        const int half = (tid >> hb) & 1;
+        const int xhp = (int)p.K + 16;                // LDS bytes of a half row
+        const unsigned char* xs = tiles + (r < p.M ? r : 0) * xhp;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            if (half == hh) {
+#pragma unroll
+                for (int j = 0; j < kXPieces; ++j) {
+                    const int q = tid + kT * j;
+                    if (q < xp) {
+                        const int t = q >> lpr;
+                        *(u32x4*)(tiles + t * xhp + 16 * (q - (t << lpr) - (hh << hb))) = XP[j];
+                    }
+                }
+            }
+            __syncthreads();
+            if ((ks >= (nks >> 1)) == (hh == 1)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t X[10];
+                    lds_group_x(xs, 4 * ks + i - hh * (p.ng >> 1), c, X);
+                    A[i] = build_group_a(X, xsh, mk);
+                }
+            }
+            __syncthreads();                          // the staged half is read
+        }
     } else {
         uint32_t XR[4][10];
         const uint16_t* xrow = p.x + (int64_t)(r < p.M ? r : 0) * p.K;
@@ -383,9 +396,9 @@ bool launch_tq_batch(const TqMatmulArgs& a, hipStream_t s, hipError_t* err) {
     p.spitch = 4 * ((int)ng / 2 + 2);
     p.lnks = ng == 16 ? 2 : ng == 32 ? 3 : 4;
     p.lxpr = p.lnks + 5;                         // K / 8 = 32 * 4-group slices
-    p.xpitch = 2 * (int)a.K + 16;
     const bool xs = a.M >= kXStageMinM;
-    if (xs && a.M * p.xpitch > kBookBytes + 2 * kTileBytes + 2 * kRedBytes) return false;
+    // staged x: half rows of K + 16 bytes in the space of the tiles and sums
+    if (xs && a.M * (a.K + 16) > 2 * kTileBytes + 2 * kRedBytes) return false;
     const int nrs = kW >> p.lnks;
     if (16 * nrs * (p.pitch + p.spitch) > kTileBytes) return false;
     // lanes per output: the outputs of a super-block (M x 16 nrs) times the
