@@ -147,8 +147,14 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
-    const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_wg;
-    const int nrows = (int)(min(r0 + (int64_t)p.rows_per_wg, p.N) - r0);
+    // read here, before the first branch, so that their argument loads go out
+    // with the others (one trip to memory before the first load, not two)
+    const int rows_per_wg = p.rows_per_wg;
+    const uint8_t* const codes = p.codes;
+    const uint16_t* const scales = p.scales;
+    asm volatile("" ::"s"(rows_per_wg), "s"(codes), "s"(scales));
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int nrows = (int)(min(r0 + (int64_t)rows_per_wg, p.N) - r0);
     const int lnks = p.lnks;                          // log2 of the 4-group slices of K (2, 3, 4)
     const int nks = 1 << lnks;
     const int ks = wave & (nks - 1), rs = wave >> lnks;
@@ -168,7 +174,7 @@ __global__ void __launch_bounds__(kT, 1) tq_batch_kernel(BatchParams p) {
     const bool is_code = tid < ncp;
     const int sp = tid - ncp;                         // scale piece when >= 0
     const bool stores = is_code || sp < (int)(sbs >> 4);
-    const uint8_t* src = is_code ? p.codes : (const uint8_t*)p.scales;
+    const uint8_t* src = is_code ? codes : (const uint8_t*)scales;
     int prow, pcol;                                   // row and byte of the piece in the super-block
     {
         const int ppr = is_code ? (int)(rb >> 4) : (p.ng >> 3);   // 16-byte pieces of a row

@@ -217,8 +217,12 @@ __global__ void __launch_bounds__(kT, 1) tq_wave_dense_kernel(WaveParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = readfirstlane(tid >> 6);
-    const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_wg;
-    const int nrows = (int)(min(r0 + (int64_t)p.rows_per_wg, p.N) - r0);
+    // read here, before the first branch, so that its argument load goes out
+    // with the others instead of after the activation loads (a second trip)
+    const int rows_per_wg = p.rows_per_wg;
+    asm volatile("" ::"s"(rows_per_wg));
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int nrows = (int)(min(r0 + (int64_t)rows_per_wg, p.N) - r0);
     const int nrq = (nrows + 3) >> 2;                 // row quads of the workgroup
     const int nkq = p.ng >> 4;                        // 16-group slices of K
     const int kq = wave % nkq, rr = wave / nkq, nrr = kW / nkq;
