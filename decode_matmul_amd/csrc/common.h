@@ -115,6 +115,16 @@ __device__ __forceinline__ bool range_ok(const Range& R) {
     return max(R.hi.x, R.hi.y) <= 0x477f && min(R.lo.x, R.lo.y) >= 0x36ff;
 }
 
+// Prefill replays: the 32-row MFMA tiles (bit i) holding a chunk flagged by
+// any of 8 converting waves, wave v's flag in byte v of f.  Converting wave v
+// covers rows 16 v .. 16 v + 15 of each 128-row half, tile v / 2 of that half.
+__device__ __forceinline__ uint32_t flag_tiles(uint64_t f) {
+    uint32_t t = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) t |= (((f >> (8 * v)) & 0xffull) != 0ull ? 1u : 0u) << (v >> 1);
+    return t;
+}
+
 // Row block of workgroup bx in a grid of nb: consecutive workgroups go to
 // the 8 XCDs in turn, so when nb is a multiple of 8 each XCD is given one
 // contiguous range of blocks (its L2 and TLB then see an eighth of the

@@ -540,6 +540,12 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
                 const uint32_t f = p.xflags[(int64_t)blockIdx.y * nslices + replay_slice(r)];
                 tmask = readfirstlane((f >> (wm * MT)) & 0xFu);
             }
+        } else {
+            // a mapped slice: wave v's flag byte covers its converted rows
+            // 16 v .. 16 v + 15 and 128 + 16 v .., in 32-row tile v / 2 of
+            // either half
+            const int w = replay_slice(r);
+            if (w < kMapSlices) tmask = (uint32_t)readfirstlane((int)flag_tiles(bad_map[w]));
         }
         store_bf16(0, S, all_bf16, -1);                 // activations only
         store_weights_hilo(S);

@@ -451,6 +451,10 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
         if constexpr (XF) {
             const uint32_t f = flag_word(fb0 + wm, w) >> (w & 1);
             tmask = (uint32_t)readfirstlane((int)((f & 1u) | ((f >> 1) & 2u) | ((f >> 2) & 4u) | ((f >> 3) & 8u)));
+        } else if (w < kMapSlices) {
+            // wave v's flag byte covers its converted rows 16 v .. 16 v + 15
+            // and 128 + 16 v .., in 32-row tile v / 2 of either half
+            tmask = (uint32_t)readfirstlane((int)flag_tiles(bad_map[w]));
         }
         store_bf16(S, w & 1);
         __syncthreads();
