@@ -200,10 +200,14 @@ def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0, x_special=F
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     xf = rng.standard_normal((M, K)).astype(np.float32)
     if x_special:
-        # activations fp16 cannot hold (tiny, huge) in a few chunks, zeros elsewhere
+        # activations fp16 cannot hold (tiny, huge) in a few chunks, zeros
+        # elsewhere, and one row entirely below 2^-17 (its products are the
+        # row's whole output, so a chunk left out of the replay would break
+        # the bound)
         xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = 3.0e-7
         xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = -7.0e4
         xf[rng.integers(0, M, 20), rng.integers(0, K, 20)] = 0.0
+        xf[(2 * M) // 3] *= np.float32(1e-7)
     xb = workloads.bf16_bits(xf)
     if planes == 1:
         c1, s1 = oracle.quantize_pack(W, G)
@@ -727,7 +731,8 @@ def test_rb_matmul_constant_worst_code(dmm, M, N, K):
 @pytest.mark.parametrize("M,N,K", BOUND_SHAPES)
 def test_rb_matmul_activations_outside_fp16(dmm, M, N, K):
     """Activations fp16 cannot hold exactly (above 65280, below 2^-17, far
-    below, exact zeros) scattered through x, and one row entirely huge."""
+    below, exact zeros) scattered through x, one row entirely huge and one
+    entirely below 2^-17."""
     rng = np.random.default_rng(3 * M + K)
     x = rng.standard_normal((M, K)).astype(np.float32)
     specials = np.array([1e5, -7e4, 3e-6, -1e-30, 0.0, 65536.0, 2.0 ** -17, 1e30],
@@ -735,6 +740,8 @@ def test_rb_matmul_activations_outside_fp16(dmm, M, N, K):
     idx = rng.integers(0, M * K, 40)
     x.reshape(-1)[idx] = specials[rng.integers(0, len(specials), 40)]
     x[M // 2] *= np.float32(1e6)
+    if M // 3 != M // 2:
+        x[M // 3] *= np.float32(1e-7)
     xb = workloads.bf16_bits(x)
     codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
     table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
@@ -1114,14 +1121,16 @@ def test_rb_matmul_ws_shapes(dmm, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(300, 64, 512), (40, 96, 1024)])
 def test_rb_matmul_ws_activations_outside_fp16(dmm, M, N, K):
-    """Chunks fp16 cannot hold (huge, tiny, a whole huge row) are flagged by
-    the pre-pass and replayed in bf16, as the in-kernel conversion does."""
+    """Chunks fp16 cannot hold (huge, tiny, a whole huge row, a whole tiny
+    row) are flagged by the pre-pass and replayed in bf16, as the in-kernel
+    conversion does."""
     rng = np.random.default_rng(5 * M + K)
     x = rng.standard_normal((M, K)).astype(np.float32)
     specials = np.array([1e5, -7e4, 3e-6, -1e-30, 0.0, 65536.0, 2.0 ** -17, 1e30], np.float32)
     idx = rng.integers(0, M * K, 40)
     x.reshape(-1)[idx] = specials[rng.integers(0, len(specials), 40)]
     x[M // 2] *= np.float32(1e6)
+    x[M // 3] *= np.float32(1e-7)
     xb = workloads.bf16_bits(x)
     codes = rng.integers(0, 243, (N, K), dtype=np.uint8)
     table = oracle.rb_table(np.array([1.0, 0.33, 0.115, 0.037, 0.012], np.float32))
@@ -1180,6 +1189,7 @@ def tq_ws_case(dmm, M, N, K, planes, ydt, seed, x_special=False):
         xf[rng.integers(0, M, 6), rng.integers(0, K, 6)] = -7.0e4
         xf[rng.integers(0, M, 20), rng.integers(0, K, 20)] = 0.0
         xf[M // 2] *= np.float32(1e6)
+        xf[M // 3] *= np.float32(1e-7)
     xb = workloads.bf16_bits(xf)
     if planes == 1:
         c1, s1 = oracle.quantize_pack(W, 64)
