@@ -45,7 +45,10 @@ constexpr int kT = 64 * kW;
 constexpr int kNB = 13;                  // code bytes per group of 64 trits
 constexpr int kMaxTasks = 4;             // tasks per wave
 constexpr int kXsPitch = 144;            // LDS bytes per staged group of 64 activations
-constexpr int kXsTok = 64 * kXsPitch;    // per token (at most 64 groups)
+// per token (at most 64 groups), padded by 64 bytes: the 16 lanes of an
+// operand read (groups 4p .. 4p + 3 of tokens 0 .. 3) then hit 16 distinct
+// 16-byte bank units (64 banks) instead of one unit per token
+constexpr int kXsTok = 64 * kXsPitch + 64;
 constexpr int kTaskStride = 68;          // floats per task: [4 lane rows][4 rows][4 tokens] + pad
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
