@@ -22,7 +22,10 @@ so host launch overhead is not timed.
                M = 1, 4, 16 (and tq_pack / tq_unpack on its matrix, per
                call), the two-plane MoE grouped GEMV, the Route B
                prefill at M = 2048 (TFLOP/s) with and without a workspace
-               (rb_matmul_ws), Route B GEMV at M = 4 and 16.
+               (rb_matmul_ws), Route B GEMV at M = 4 and 16.  One entry
+               is context, not this library: the vendor fp16 GEMM of the
+               prefill's shape with nothing to decode
+               (context_vendor_fp16_gemm_M2048).
 
 Inputs are the seeded synthetic workloads of workloads.py; the pages'
 published numbers are end-to-end decode rates on other hardware, so
@@ -495,6 +498,18 @@ def run_extras(torch, dmm, workloads, to_dev, use_graph, args):
         sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
         res["routeb_prefill_ws_M2048"] = _prefill_rec(sec, flops)
         del ws
+        # context only, not this library: the vendor fp16 GEMM (torch.matmul,
+        # hipBLASLt) of the same shape with weights already in fp16, i.e. the
+        # rate of a plain GEMM on this part with nothing to decode
+        wf = torch.randn(8192, 8192, device=dev, dtype=torch.float16).t().contiguous()
+        xf = torch.randn(2048, 8192, device=dev, dtype=torch.float16)
+        yf = torch.empty((2048, 8192), dtype=torch.float16, device=dev)
+        fn = lambda: torch.matmul(xf, wf, out=yf)
+        sec = _timed_launches(torch, fn, 1, use_graph, reps=10, warmup=2)
+        rec = _prefill_rec(sec, flops)
+        rec["what"] = "torch.matmul fp16 2048x8192 @ 8192x8192, no decode (vendor library, context)"
+        res["context_vendor_fp16_gemm_M2048"] = rec
+        del wf, xf, yf
 
     if "blocks" in sel:
         progress("extra: routeb_blocks (one code book per 32 rows)")
