@@ -483,6 +483,10 @@ __global__ void __launch_bounds__(kThreads, 1) rb_prefill_kernel(Params p) {
     load_frag(0, 0, 0, F0);
 #pragma unroll 1
     for (int s = 0; s < nslices; ++s) {
+        // ask the scheduler to interleave the MFMAs with the LDS reads and
+        // writes around them (strategy 0); the order of the arithmetic is
+        // unchanged, and so is every output bit
+        __builtin_amdgcn_iglp_opt(0);
         const int buf = s & 1;
         load_frag(buf, buf, 1, F1);        // slice s, second K-step
         mfma_frag(F0, true, 0xFu);

@@ -383,6 +383,9 @@ __global__ void __launch_bounds__(kThreads, 1) tq_prefill_kernel(Params p) {
     load_frag(0, 0, 0, F0);
     auto step = [&](auto Hc, int s) {
         constexpr int H = decltype(Hc)::value;
+        // the scheduler interleaves the MFMAs with the LDS traffic around
+        // them (strategy 0); the arithmetic and its order are unchanged
+        __builtin_amdgcn_iglp_opt(0);
         load_frag(H, H, 1, F1);            // slice s, second K-step
         mfma_frag(F0, true, 0xFu);
         __syncthreads();                   // every wave is done reading buffer H
