@@ -209,6 +209,86 @@ unpack_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc
     }
 }
 
+// Unpack at G = 64 with whole groups (K % 64 == 0), so that group g's 64
+// values are elements 64 g .. 64 g + 63 of the output.  A wave takes 8
+// groups (104 code bytes, 512 values) at a time; lane (g, q) writes values
+// 8 q .. 8 q + 7 of its group as one 16-byte piece (two for fp32).  Those are
+// digits o .. o + 7 of the 15 held by code bytes f, f + 1, f + 2 of the group
+// (f = floor(8 q / 5), o = 8 q - 5 f; the third byte, needed when o >= 3,
+// is clamped into the group).  Each byte's five digits come from a
+// 256-entry table (2 bits a digit; bytes 243..255 decode as 121, all
+// zeros).  A digit d gives the value bits (s ^ sign) & mask: mask clears
+// d = 1 (t = 0), sign flips d = 0 (t = -1), so each value is exactly
+// s * t rounded as the general kernel rounds it.  Every code byte of a
+// group lies in some lane's window, and lane q = 7's window holds the
+// padding digit (digit 4 of byte 12), so the status flags match too.
+constexpr int kUn64Threads = 256;
+typedef unsigned short u16x2un __attribute__((ext_vector_type(2)));
+
+__global__ void __launch_bounds__(kUn64Threads)
+unpack64_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                int64_t groups, void* __restrict__ out, int out_dtype, int32_t* st) {
+    __shared__ uint32_t dig[256];
+    const int tid = threadIdx.x;
+    {
+        uint32_t v = tid > 242 ? 121u : (uint32_t)tid, e = 0;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            e |= (v % 3u) << (2 * i);
+            v /= 3u;
+        }
+        dig[tid] = e;
+    }
+    __syncthreads();
+    const int lane = tid & 63;
+    const uint32_t q = (uint32_t)(lane & 7);
+    const uint32_t f = (8u * q) / 5u, o = 8u * q - 5u * f;
+    const uint32_t f3 = f + 2u < 12u ? f + 2u : 12u;
+    int flags = 0;
+    const int64_t tasks = (groups + 7) >> 3;
+    const int64_t stride = (int64_t)gridDim.x * (kUn64Threads / 64);
+    for (int64_t t = (int64_t)blockIdx.x * (kUn64Threads / 64) + (tid >> 6); t < tasks; t += stride) {
+        const int64_t g = 8 * t + (lane >> 3);
+        if (g >= groups) continue;
+        const uint8_t* cb = codes + 13 * g;
+        const uint32_t b0 = cb[f], b1 = cb[f + 1], b2 = cb[f3];
+        if (b0 > 242u || b1 > 242u || b2 > 242u) flags |= TQ_DATA_CODE;
+        const uint32_t w = (dig[b0] | (dig[b1] << 10) | (dig[b2] << 20)) >> (2u * o);
+        if (q == 7u && ((w >> 16) & 3u) != 1u) flags |= TQ_DATA_PADDING;
+        const float sf = f16_bits_to_f32(scales[g]);
+        if (out_dtype == TQ_BF16) {
+            const uint32_t sb = f32_to_bf16_rne(sf);
+            const uint32_t s2 = sb | (sb << 16);
+            u32x4 v;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                // digits 2p (low half) and 2p + 1 (high half)
+                const uint32_t x = w >> (4 * p);
+                const uint32_t d = (x & 3u) | ((x << 14) & 0x30000u);
+                // per 16-bit half: (d & 1) - 1 is 0 where d == 1, else 0xFFFF
+                const uint32_t mask = __builtin_bit_cast(
+                    uint32_t, __builtin_bit_cast(u16x2un, d & 0x00010001u) - (u16x2un){1, 1});
+                const uint32_t sign = ((d ^ 0x00020002u) & 0x00020002u) << 14;
+                v[p] = (s2 ^ sign) & mask;
+            }
+            *(u32x4*)((uint16_t*)out + 64 * g + 8 * q) = v;
+        } else {
+            const uint32_t s32 = __builtin_bit_cast(uint32_t, sf);
+            u32x4 v[2];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t d = (w >> (2 * k)) & 3u;
+                const uint32_t mask = (d & 1u) - 1u;                     // 0 where d == 1
+                const uint32_t sign = ((d ^ 2u) & 2u) << 30;
+                v[k >> 2][k & 3] = (s32 ^ sign) & mask;
+            }
+            *(u32x4*)((float*)out + 64 * g + 8 * q) = v[0];
+            *(u32x4*)((float*)out + 64 * g + 8 * q + 4) = v[1];
+        }
+    }
+    if (flags) atomic_or_status(st, flags);
+}
+
 }  // namespace
 
 hipError_t launch_status_clear(int32_t* d_status, hipStream_t s) {
@@ -237,6 +317,15 @@ hipError_t launch_unpack(const uint8_t* codes, const uint16_t* scales, int64_t r
     int nb = (G + 4) / 5;
     int64_t groups = rows * (int64_t)ng;
     if (groups == 0) return hipSuccess;
+    if (G == 64 && K % 64 == 0 && ((uintptr_t)out & 15) == 0) {
+        // whole groups of 64: the wave-per-8-groups kernel, a grid of a few
+        // workgroups per compute unit striding over the groups
+        const int64_t wgs = (groups + 8 * (kUn64Threads / 64) - 1) / (8 * (kUn64Threads / 64));
+        const int64_t cap = 8 * (int64_t)compute_unit_count();
+        hipLaunchKernelGGL(unpack64_kernel, dim3((unsigned)(wgs < cap ? wgs : cap)),
+                           dim3(kUn64Threads), 0, s, codes, scales, groups, out, out_dtype, d_status);
+        return hipGetLastError();
+    }
     const int gpw = groups_per_wg(G);
     int64_t blocks = (groups + gpw - 1) / gpw;
     hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(kPackThreads), 0, s, codes,

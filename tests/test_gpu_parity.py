@@ -193,6 +193,79 @@ def test_unpack_rejects_bad_bytes(dmm):
     assert int(host(st)[0]) == 4
 
 
+@pytest.mark.parametrize("rows,K", [(1, 64), (37, 320), (3, 4096), (129, 1024), (1000, 128)])
+def test_unpack_whole_groups(dmm, rows, K):
+    """G = 64 with K % 64 == 0 (the wave-per-8-groups kernel): group counts
+    that end inside a wave's 8 groups, one group, many workgroups; fp32 and
+    bf16 bit-exact against the oracle, and an output view offset by one
+    element (not 16-byte aligned) through the general kernel."""
+    W = (np.random.default_rng(rows * 7 + K).standard_normal((rows, K)) * 0.02).astype(np.float32)
+    W[0, :64] = 0.0                                     # a zero-scale group
+    c, s = oracle.quantize_pack(W, 64)
+    ref = oracle.unpack(c, s, K, 64)
+    for odt in (torch.float32, torch.bfloat16):
+        for off in (0, 1):
+            say(f"tq_unpack whole groups {rows}x{K} {odt} offset {off}")
+            buf = torch.empty(rows * K + off, dtype=odt, device=DEV)
+            out = buf[off:]
+            st = dmm.tq_unpack(dev(c), dev(bits16(s)), rows, K, 64, out)
+            assert int(host(st)[0]) == 0
+            if odt == torch.float32:
+                got = host(out).reshape(rows, K).view(np.uint32)
+                assert np.array_equal(got, ref.astype(np.float32).view(np.uint32))
+            else:
+                got = host(out.view(torch.int16)).reshape(rows, K).view(np.uint16)
+                assert np.array_equal(got, oracle.f64_to_bf16_bits(ref))
+
+
+def test_unpack_whole_groups_flags_every_byte(dmm):
+    """Every code byte position of a G = 64 group, set to an invalid value in
+    turn, is reported and decodes to zeros, with the rest of the package
+    unchanged; a padding digit is reported in any group of a wave."""
+    rows, K = 5, 192                                    # 15 groups: two waves' worth
+    W = (np.random.default_rng(17).standard_normal((rows, K)) * 0.02).astype(np.float32)
+    c, s = oracle.quantize_pack(W, 64)
+    ref = oracle.unpack(c, s, K, 64).astype(np.float32)
+    for r, g in ((0, 0), (2, 1), (4, 2)):
+        for i in range(13):
+            c2 = c.copy()
+            c2[r, g, i] = 243 + (i % 13)
+            out = torch.empty((rows, K), dtype=torch.float32, device=DEV)
+            say(f"tq_unpack whole groups invalid byte {i} of group ({r}, {g})")
+            st = dmm.tq_unpack(dev(c2), dev(bits16(s)), rows, K, 64, out)
+            assert int(host(st)[0]) == 2
+            got = host(out)
+            lo, hi = 64 * g + 5 * i, min(64 * g + 5 * i + 5, 64 * (g + 1))
+            mask = np.ones((rows, K), bool)
+            mask[r, lo:hi] = False
+            assert np.array_equal(got[mask], ref[mask])
+            assert np.all(got[r, lo:hi] == 0)
+    for r, g in ((0, 2), (3, 0), (4, 2)):
+        c3 = c.copy()
+        c3[r, g, 12] = (c3[r, g, 12] % 81) + 162            # padding digit -> 2
+        out = torch.empty((rows, K), dtype=torch.bfloat16, device=DEV)
+        say(f"tq_unpack whole groups bad padding in group ({r}, {g})")
+        st = dmm.tq_unpack(dev(c3), dev(bits16(s)), rows, K, 64, out)
+        assert int(host(st)[0]) == 4
+
+
+def test_unpack_full_ternary_gemv(dmm):
+    """The 14336 x 4096 package of the GEMV workload, bf16 and fp32, bit-exact
+    over every element."""
+    W = workloads.ternary_gemv()["W"]
+    c, s = oracle.quantize_pack(W, 64)
+    ref = oracle.unpack(c, s, 4096, 64)
+    for odt in (torch.bfloat16, torch.float32):
+        say(f"tq_unpack ternary_gemv 14336x4096 {odt}")
+        out = torch.empty((14336, 4096), dtype=odt, device=DEV)
+        st = dmm.tq_unpack(dev(c), dev(bits16(s)), 14336, 4096, 64, out)
+        assert int(host(st)[0]) == 0
+        if odt == torch.float32:
+            assert np.array_equal(host(out).view(np.uint32), ref.astype(np.float32).view(np.uint32))
+        else:
+            assert np.array_equal(host(out.view(torch.int16)).view(np.uint16), oracle.f64_to_bf16_bits(ref))
+
+
 # ------------------------------------------------------------------ tq_matmul
 
 def tq_case(dmm, M, N, K, G, planes, ydt, seed, code_off=0, x_off=0, x_special=False):
