@@ -221,7 +221,9 @@ unpack_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ sc
 // d = 1 (t = 0), sign flips d = 0 (t = -1), so each value is exactly
 // s * t rounded as the general kernel rounds it.  Every code byte of a
 // group lies in some lane's window, and lane q = 7's window holds the
-// padding digit (digit 4 of byte 12), so the status flags match too.
+// padding digit (digit 4 of byte 12), so the status flags match too.  The
+// output is written with streaming (nontemporal) stores: nothing reads it
+// back in this kernel, and the write stream then runs about a third faster.
 constexpr int kUn64Threads = 256;
 typedef unsigned short u16x2un __attribute__((ext_vector_type(2)));
 
@@ -271,7 +273,7 @@ unpack64_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ 
                 const uint32_t sign = ((d ^ 0x00020002u) & 0x00020002u) << 14;
                 v[p] = (s2 ^ sign) & mask;
             }
-            *(u32x4*)((uint16_t*)out + 64 * g + 8 * q) = v;
+            __builtin_nontemporal_store(v, (u32x4*)((uint16_t*)out + 64 * g + 8 * q));
         } else {
             const uint32_t s32 = __builtin_bit_cast(uint32_t, sf);
             u32x4 v[2];
@@ -282,8 +284,8 @@ unpack64_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ 
                 const uint32_t sign = ((d ^ 2u) & 2u) << 30;
                 v[k >> 2][k & 3] = (s32 ^ sign) & mask;
             }
-            *(u32x4*)((float*)out + 64 * g + 8 * q) = v[0];
-            *(u32x4*)((float*)out + 64 * g + 8 * q + 4) = v[1];
+            __builtin_nontemporal_store(v[0], (u32x4*)((float*)out + 64 * g + 8 * q));
+            __builtin_nontemporal_store(v[1], (u32x4*)((float*)out + 64 * g + 8 * q + 4));
         }
     }
     if (flags) atomic_or_status(st, flags);
