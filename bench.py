@@ -46,7 +46,7 @@ HBM_PEAK_GBS = 8000.0
 # copy read and write 512 MiB), in profiles/hbm_traffic_rb_gemv_tq_wave.md.
 # The figure belongs to the kernel source it was measured on: any other
 # source of rb_gemv.hip reports null.
-MEASURED_TRAFFIC = {"rb_gemv.hip": ("9d8a18834a440de8", 67360886)}
+MEASURED_TRAFFIC = {"rb_gemv.hip": ("9908ab656a4fabaa", 67668937)}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "packed matmul: weight GB/s vs HBM peak at M=1–16; TFLOP/s at M=2048"
 

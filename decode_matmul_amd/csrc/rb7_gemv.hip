@@ -137,7 +137,7 @@ rb7_gemv_tiled_kernel(Params p) {
     };
     auto fetch = [&](int64_t t, Stage& S) {
         const int64_t tc = min(t, ntiles - 1);
-        S.c = *(const u32x4*)(grow + tc * kTileRowBytes);
+        S.c = __builtin_nontemporal_load((const u32x4*)(grow + tc * kTileRowBytes));   // read once: streaming
         const u32x4a* xp = (const u32x4a*)(xrow + tc * kTileK);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {

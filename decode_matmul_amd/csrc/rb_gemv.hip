@@ -371,7 +371,8 @@ rb_gemv_tiled_kernel(Params p) {
     };
     auto fetch = [&](int64_t t, Stage& S) {
         const int64_t tc = min(t, ntiles - 1);
-        S.c = *(const u32x4a*)(grow + tc * kTileK);
+        // the codes are read once: a streaming (nontemporal) load
+        S.c = __builtin_nontemporal_load((const u32x4a*)(grow + tc * kTileK));
         const u32x4a* xp = (const u32x4a*)((XS ? xsrc : xrow) + tc * kTileK);
         u32x4a a = xp[0], b = xp[1];
         S.X[0] = a.x; S.X[1] = a.y; S.X[2] = a.z; S.X[3] = a.w;
