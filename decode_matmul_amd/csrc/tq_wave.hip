@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(kT, 1) tq_wave_dense_kernel(WaveParams p) {
             const uint8_t* cb = p.codes[pl] + row0 * rb;
             const uint8_t* sb = (const uint8_t*)p.scales[pl] + row0 * 2 * p.ng;
             C[t][pl] = __builtin_nontemporal_load((const u32x4a*)(cb + co));
-            S[t][pl] = *(const uint16_t*)(sb + so);
+            S[t][pl] = __builtin_nontemporal_load((const uint16_t*)(sb + so));   // read once
         }
     };
     issue(0);
